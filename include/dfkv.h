@@ -1,0 +1,314 @@
+/*
+ * dfkv.h -- C ABI of libdfkv: the decode-step context-KV update of a
+ * DFlash / DSpark block drafter on one MI355X (gfx950) GPU.
+ *
+ * One step takes the target model's captured hidden states for the K+1
+ * verified tokens of every generation request and
+ *   1. projects them into every drafter layer's context K/V (or MLA latent):
+ *      fc over the concatenated target layers, hidden_norm (RMSNorm), one
+ *      GEMM stacked across all drafter layers, per-layer k_norm with stacked
+ *      weights and one shared eps, and RoPE read from one cos/sin cache;
+ *   2. does the per-request bookkeeping: bonus token, query and context
+ *      positions, embedding ids, the rejected-row mask, the clamp to the
+ *      request's allocation, the block-table page lookup, the ctx_len advance
+ *      with the dummy-slot reset, and seq_lens;
+ *   3. writes the accepted rows into every layer's paged pool.
+ *
+ * Sources (page titles and sections):
+ *  [P20550]  TensorRT-LLM PR #20550 "DFlash / MLA DSpark: fuse the decode-step
+ *            drafter bookkeeping into Triton kernels": sections
+ *            TLLM_DFLASH_FUSED_PROLOGUE, TLLM_DFLASH_OVERLAP_CONTEXT_PROJECTION,
+ *            Test Coverage; and the downstream commit quoted on that page
+ *            ("per-request bookkeeping ... one kernel stores the context
+ *            latents of every drafter layer").
+ *  [P13995]  TensorRT-LLM PR #13995 "DFlash performance optimizations":
+ *            commits "migrate draft path to per-layer cached K/V pool",
+ *            "fuse cross-layer k_norm", "match RoPE between context and query
+ *            for YaRN", "fuse query-input build", "drop K-1 filler tokens".
+ *  [I20548]  TensorRT-LLM issue #20548 "DFlash / MLA DSpark decode spends
+ *            ~0.2 ms per step in small bookkeeping kernels": Description.
+ *
+ * Conventions for every call
+ *  - All tensors are device pointers (hipMalloc'd memory) unless a field
+ *    says "host".  bf16 tensors are raw IEEE bfloat16 bit patterns.  The
+ *    caller owns every buffer; the library never allocates device memory
+ *    and keeps no pointer after a call returns.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream).  No call synchronises the host, allocates, or reads
+ *    the environment, so every call may be captured into a hipGraph; a
+ *    captured graph keeps the pointers and sizes of capture time.
+ *  - Host-side validation runs before any launch.  On any status other than
+ *    DFKV_OK nothing was launched and no device memory was touched, except
+ *    DFKV_ERR_HIP, which reports a launch failure.
+ *  - Bad device *values* (a negative or out-of-range page, n_acc > W, a
+ *    position past the block table or the allocation) are not errors: the
+ *    write predicate of dfkv_paged_store turns them into "no write", and no
+ *    access goes out of bounds.
+ *  - Row n of a step is token i = n % W of request r = n / W, with
+ *    W = geom.width = K+1 (uniform verify width, [P13995] "drop K-1 filler
+ *    tokens"; strict acceptance of a uniform-width draft, [P20550]
+ *    downstream commit).
+ */
+#ifndef DFKV_H
+#define DFKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *dfkv_stream_t; /* a hipStream_t */
+
+typedef enum dfkv_status {
+    DFKV_OK = 0,
+    DFKV_ERR_NULL = -1,      /* a required pointer is NULL */
+    DFKV_ERR_SHAPE = -2,     /* unsupported or inconsistent sizes */
+    DFKV_ERR_LAYOUT = -3,    /* misaligned pointer, too-small stride, bad pool strides */
+    DFKV_ERR_ALIAS = -4,     /* an output overlaps an input it must not overlap */
+    DFKV_ERR_WORKSPACE = -5, /* workspace too small */
+    DFKV_ERR_HIP = -6        /* a kernel launch failed */
+} dfkv_status;
+
+enum { DFKV_GQA = 0, DFKV_MLA = 1 };
+enum { DFKV_MAX_LAYERS = 32 };
+
+/* dfkv_project flags */
+enum { DFKV_FUSE_NORM_ROPE = 1u };
+
+/* Geometry of the drafter and of the step.
+ *  GQA: each layer's stacked projection row is [2][n_kv_heads][head_dim]
+ *       (index 0 = K, 1 = V); rope_dim must equal head_dim (full rotation);
+ *       head_dim in {64, 128, 256}.
+ *  MLA: each layer's row is [latent_dim + rope_dim]; n_kv_heads = 1,
+ *       head_dim = 0; latent_dim and latent_dim + rope_dim multiples of 64,
+ *       rope_dim even and <= 128 ([P20550] single-latent pool geometry
+ *       shared by all layers).
+ *  n_tgt * tgt_hidden and hidden: multiples of 128.
+ *  eps: one eps for hidden_norm and the k/latent norm ([P13995] "fuse
+ *  cross-layer k_norm": all layers share one variance epsilon). */
+typedef struct dfkv_geom {
+    int32_t kind;
+    int32_t n_tgt;
+    int32_t tgt_hidden;
+    int32_t hidden;
+    int32_t n_layers;
+    int32_t n_kv_heads;
+    int32_t head_dim;
+    int32_t latent_dim;
+    int32_t rope_dim;
+    float eps;
+    int32_t page_size;
+    int32_t width;      /* W = K+1 verify rows per request */
+    int32_t block_size; /* drafter block: query length of the next draft block */
+} dfkv_geom;
+
+/* Drafter weights, nn.Linear layout [out][in] row-major, bf16, 16-byte aligned.
+ *  w_fc    [hidden][n_tgt * tgt_hidden]
+ *  w_hnorm [hidden]
+ *  w_kv    [n_layers * per_layer][hidden]  (per_layer = 2*nkv*hd or R+P)
+ *  w_knorm [n_layers][head_dim] (GQA k_norm) or [n_layers][latent_dim] (MLA) */
+typedef struct dfkv_weights {
+    const void *w_fc;
+    const void *w_hnorm;
+    const void *w_kv;
+    const void *w_knorm;
+} dfkv_weights;
+
+/* Request state of one step (all device arrays).
+ *  ctx_len_in   [B] int32  context length before the step
+ *  n_acc        [B] int32  accepted rows this step (a prefix of the W rows)
+ *  alloc_limit  [B] int32  tokens the request may hold (pages allocated * page_size,
+ *                          with any max_ctx ceiling folded in by the caller)
+ *  is_dummy     [B] uint8  padded dummy slot: no writes, ctx_len reset to 0
+ *  row_valid    [B*W] uint8 or NULL: extra per-row rejection mask
+ *  block_table  element (r, j) at r*bt_row_stride + j, j < bt_cols (int32 page ids)
+ *  accepted_tokens element (r, t) at r*acc_stride_req + t*acc_stride_tok (int32;
+ *                  any strided view, e.g. a transposed [W][B] tensor)
+ *  mask_token_id   id of the drafter's mask token */
+typedef struct dfkv_requests {
+    int32_t n_reqs;
+    const int32_t *ctx_len_in;
+    const int32_t *n_acc;
+    const int32_t *alloc_limit;
+    const uint8_t *is_dummy;
+    const uint8_t *row_valid;
+    const int32_t *block_table;
+    int64_t bt_row_stride;
+    int32_t bt_cols;
+    const int32_t *accepted_tokens;
+    int64_t acc_stride_req;
+    int64_t acc_stride_tok;
+    int32_t mask_token_id;
+} dfkv_requests;
+
+/* Per-layer paged pools (bf16).  k[l], v[l]: device base pointers, 16-byte
+ * aligned (MLA: k[l] is the latent pool, v unused).  Element (page, off, head, e)
+ * of a GQA pool is at page*stride_page + off*stride_slot + head*stride_head + e;
+ * a token's MLA latent row (R+P elements) is at page*stride_page + off*stride_slot.
+ * Strides in elements, multiples of 8; e is contiguous.  Both the
+ * [page][slot][head][dim] and the [page][head][slot][dim] layouts are expressible. */
+typedef struct dfkv_pool {
+    void *k[DFKV_MAX_LAYERS];
+    void *v[DFKV_MAX_LAYERS];
+    int64_t stride_page;
+    int64_t stride_slot;
+    int64_t stride_head;
+    int32_t num_pages;
+} dfkv_pool;
+
+/* Bookkeeping outputs (device arrays; none may overlap an input).
+ *  slot        [B*W] int64  page*page_size + offset of each written row, -1 if none
+ *  write_mask  [B*W] uint8  1 iff the row was written into the pools
+ *  c_pos       [B*W] int32  context / RoPE position ctx_len_in + i
+ *  bonus       [B]   int32  last accepted token, accepted[r][clamp(n_acc,1,W)-1]
+ *  emb_ids     [B*block_size] int32  [bonus, mask_token_id x (block_size-1)]
+ *  q_pos       [B*block_size] int32  ctx_len_out + j
+ *  ctx_len_out [B]   int32  dummy ? 0 : min(ctx_len_in + n_acc, alloc_limit)
+ *                           (also the advertised context length)
+ *  seq_len     [B]   int32  ctx_len_out + block_size */
+typedef struct dfkv_outputs {
+    int64_t *slot;
+    uint8_t *write_mask;
+    int32_t *c_pos;
+    int32_t *bonus;
+    int32_t *emb_ids;
+    int32_t *q_pos;
+    int32_t *ctx_len_out;
+    int32_t *seq_len;
+} dfkv_outputs;
+
+/* RoPE parameters.  yarn = 0: plain RoPE (RoFormer), inverse frequencies
+ * theta^(-2i/rot).  yarn = 1: YaRN "NTK-by-parts" in the HF formulation
+ * (correction range from beta_fast / beta_slow over orig_ctx, floor/ceil
+ * only if truncate, linear ramp blending inv and inv/factor, attention factor
+ * 0.1*ln(factor)+1 applied to cos and sin).  [P13995] "match RoPE between
+ * context and query for YaRN": context K and query K must read one cache. */
+typedef struct dfkv_rope {
+    double theta;
+    int32_t rot;
+    int32_t yarn;
+    double factor;
+    double orig_ctx;
+    double beta_fast;
+    double beta_slow;
+    int32_t truncate;
+} dfkv_rope;
+
+/* Human-readable name of a status. */
+const char *dfkv_status_string(dfkv_status s);
+
+/* Library version string (static storage). */
+const char *dfkv_version(void);
+
+/* After a call returned DFKV_ERR_HIP: the HIP runtime's description of the
+ * failed launch (per host thread; static storage). */
+const char *dfkv_hip_error_string(void);
+
+/* Bytes of workspace dfkv_project / dfkv_step need for n_reqs requests
+ * (split-K partials, row statistics, tile tickets).  Writes *bytes.
+ * Errors: NULL if g or bytes is NULL; SHAPE for an unsupported geometry. */
+dfkv_status dfkv_workspace_size(const dfkv_geom *g, int32_t n_reqs, size_t *bytes);
+
+/* Prepare a workspace once after allocating it (zeroes it with a kernel, not a
+ * memset).  The workspace starts with the split-K tile tickets, at offsets that
+ * depend only on the geometry; every dfkv_project / dfkv_step leaves them zeroed
+ * again, so one workspace sized for the largest batch serves every batch size.
+ * Two calls that share one workspace must not run concurrently.
+ * Errors: NULL; LAYOUT (not 16-byte aligned); HIP. */
+dfkv_status dfkv_workspace_init(void *ws, size_t ws_bytes, dfkv_stream_t stream);
+
+/* Build the one cos/sin cache that context K (this library) and query K (the
+ * drafter) both read.  cos_sin: device float [cache_len][rot]; row p holds
+ * m*cos(p*inv_i) for i < rot/2, then m*sin(p*inv_i).  Angles and values are
+ * computed in fp64 on the GPU and stored as fp32 (an fp32 angle at position
+ * 4e5 would be off by several hundredths of a radian).  [P13995] "match RoPE
+ * between context and query for YaRN".
+ * Errors: NULL; SHAPE (rot odd or <= 0, cache_len <= 0, factor <= 0 under
+ * YaRN, theta <= 1); LAYOUT (cos_sin not 4-byte aligned); HIP. */
+dfkv_status dfkv_rope_cache_build(const dfkv_rope *rope, float *cos_sin, int32_t cache_len,
+                                  dfkv_stream_t stream);
+
+/* Context projection of all N = n_reqs*W rows ([P20550]
+ * TLLM_DFLASH_OVERLAP_CONTEXT_PROJECTION: fc + hidden_norm + latent GEMM +
+ * RMSNorm/RoPE; [P13995] one GEMM stacked across drafter layers).
+ *   f  = bf16(hidden . w_fc^T)                         [N][hidden]
+ *   g  = bf16(w_hnorm * f / sqrt(mean(f^2) + eps))      (hidden_norm)
+ *   y  = bf16(g . w_kv^T)                               [N][O]
+ * With DFKV_FUSE_NORM_ROPE, kv_out = y with k_norm and RoPE applied as in
+ * dfkv_norm_rope; without it, kv_out = y.
+ * Reads only hidden, the weights, cos_sin and the pre-step ctx_len_in (never
+ * n_acc), so it may run on a side stream overlapped with sample/accept.
+ *  hidden: bf16, row n at n*hidden_row_stride, first n_tgt*tgt_hidden
+ *          elements used; rows 16-byte aligned.
+ *  kv_out: bf16 [N][O] contiguous, 16-byte aligned; must not overlap hidden,
+ *          the weights, cos_sin or ws.
+ *  cos_sin/cache_len: needed only with DFKV_FUSE_NORM_ROPE.
+ *  ws: >= dfkv_workspace_size bytes, prepared by dfkv_workspace_init.
+ * Errors: NULL, SHAPE, LAYOUT, ALIAS, WORKSPACE, HIP. */
+dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
+                         int64_t hidden_row_stride, int32_t n_reqs, const int32_t *ctx_len_in,
+                         const float *cos_sin, int32_t cache_len, void *kv_out, uint32_t flags,
+                         void *ws, size_t ws_bytes, dfkv_stream_t stream);
+
+/* k_norm (or latent norm) and RoPE in place on a stacked projection y.
+ * GQA, every K head (l, h) of every row: u = bf16(w_knorm[l] * y / sqrt(mean(y^2)+eps)),
+ * then NeoX half-split rotation at pos = ctx_len_in[r] + i from cache row
+ * min(max(pos,0), cache_len-1):  k[j] = bf16(u[j]c_j - u[j+h]s_j),
+ * k[j+h] = bf16(u[j+h]c_j + u[j]s_j), h = rot/2.  V heads are untouched.
+ * MLA, every layer: the latent_dim part is RMSNorm'ed with w_knorm[l], the
+ * rope_dim part is rotated (no norm).  ([P13995] "fuse cross-layer k_norm":
+ * one RMSNorm over [N, L, nkv, hd] times the stacked weights; "match RoPE
+ * between context and query for YaRN".)
+ *  kv: bf16 [N][O] contiguous, 16-byte aligned.
+ * Errors: NULL, SHAPE, LAYOUT, ALIAS (kv overlapping cos_sin or w_knorm), HIP. */
+dfkv_status dfkv_norm_rope(const dfkv_geom *g, const void *w_knorm, int32_t n_reqs,
+                           const int32_t *ctx_len_in, const float *cos_sin, int32_t cache_len,
+                           void *kv, dfkv_stream_t stream);
+
+/* Paged store of the gen tokens' context K/V ([P20550] TLLM_DFLASH_FUSED_PROLOGUE:
+ * rejected-row mask, clamp to the request's allocation, page lookup, write to
+ * every layer; downstream commit: pool entries outside the step's destinations
+ * stay unchanged, every destination is written).  For row n (request r, token i),
+ * pos = ctx_len_in[r] + i, the row is written iff
+ *   !is_dummy[r] && i < n_acc[r] && (row_valid == NULL || row_valid[n])
+ *   && 0 <= pos < alloc_limit[r] && pos/page_size < bt_cols
+ *   && 0 <= page < num_pages, page = block_table[r][pos/page_size];
+ * then every layer l receives the row's layer-l K and V (GQA) or latent (MLA)
+ * at (page, pos % page_size).  slot_out/write_mask_out as in dfkv_outputs.
+ *  kv: bf16 [N][O] (the output of dfkv_project with DFKV_FUSE_NORM_ROPE).
+ * Errors: NULL, SHAPE, LAYOUT (pool alignment/strides), ALIAS (outputs over
+ * inputs or pools), HIP. */
+dfkv_status dfkv_paged_store(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
+                             const dfkv_pool *pool, int64_t *slot_out, uint8_t *write_mask_out,
+                             dfkv_stream_t stream);
+
+/* Per-request advance ([P20550] TLLM_DFLASH_FUSED_PROLOGUE: bonus token, query
+ * and context positions, embedding ids, ctx_len advance with the clamp and the
+ * dummy-slot reset, advertised context length; downstream commit: seq_lens;
+ * [P13995] "fuse query-input build": positions by broadcast-add, embedding ids
+ * [bonus, mask...]).  Writes out->c_pos, bonus, emb_ids, q_pos, ctx_len_out,
+ * seq_len (slot and write_mask are ignored and may be NULL).
+ * ctx_len_out must not overlap ctx_len_in (no in-place advance).
+ * Errors: NULL, SHAPE, ALIAS, HIP. */
+dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfkv_outputs *out,
+                         dfkv_stream_t stream);
+
+/* dfkv_paged_store and dfkv_advance in one coalesced launch; writes every
+ * field of *out.  Errors as the two calls. */
+dfkv_status dfkv_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
+                               const dfkv_pool *pool, const dfkv_outputs *out, dfkv_stream_t stream);
+
+/* One whole step: dfkv_project(DFKV_FUSE_NORM_ROPE) into kv_out, then
+ * dfkv_store_advance.  ctx_len_in is taken from req.  Errors as the parts. */
+dfkv_status dfkv_step(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
+                      int64_t hidden_row_stride, const dfkv_requests *req, const float *cos_sin,
+                      int32_t cache_len, void *kv_out, const dfkv_pool *pool, const dfkv_outputs *out,
+                      void *ws, size_t ws_bytes, dfkv_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFKV_H */

@@ -57,6 +57,8 @@ class Oracle:
                 raise FileNotFoundError(path)
         self.path = path
         L = C.CDLL(path)
+        L.dfkv_oracle_threads.argtypes = []
+        L.dfkv_oracle_threads.restype = C.c_int
         L.dfkv_oracle_bf16_to_f64.argtypes = [C.c_uint16]
         L.dfkv_oracle_bf16_to_f64.restype = C.c_double
         L.dfkv_oracle_f64_to_bf16.argtypes = [C.c_double]
@@ -77,6 +79,9 @@ class Oracle:
                    "dfkv_oracle_bookkeeping", "dfkv_oracle_store"):
             getattr(L, fn).restype = None
         self.lib = L
+
+    def threads(self) -> int:
+        return int(self.lib.dfkv_oracle_threads())
 
     # -- scalars -----------------------------------------------------------
     def bf16_to_f64(self, h: int) -> float:

@@ -47,6 +47,20 @@
 
 #define EXPORT __attribute__((visibility("default")))
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the oracle's parallel loops use (1 without OpenMP). */
+EXPORT int dfkv_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* bf16 <-> fp64                                                             */
 /* ------------------------------------------------------------------------ */

@@ -1,0 +1,559 @@
+// dfkv_api.hip -- the C ABI of libdfkv: host-side validation, workspace
+// planning and kernel dispatch.  Every check runs before the first launch, so
+// a refused call launches nothing and writes nothing.
+#include <string.h>
+
+#include "dfkv_internal.hpp"
+
+using namespace dfkv;
+
+namespace {
+
+thread_local hipError_t g_last_hip_error = hipSuccess;
+
+dfkv_status hip_status(hipError_t e) {
+    if (e == hipSuccess) return DFKV_OK;
+    g_last_hip_error = e;
+    return DFKV_ERR_HIP;
+}
+
+constexpr int kSkinnyMaxRows = 64;   // M = B*W handled by the weight-streaming split-K path
+constexpr int kTargetItems = 768;    // split-K work items aimed for per GEMM (256 CUs x 3)
+
+bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool al4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int per_layer(const dfkv_geom *g) {
+    return g->kind == DFKV_GQA ? 2 * g->n_kv_heads * g->head_dim : g->latent_dim + g->rope_dim;
+}
+int64_t out_dim(const dfkv_geom *g) { return (int64_t)g->n_layers * per_layer(g); }
+int64_t k_in(const dfkv_geom *g) { return (int64_t)g->n_tgt * g->tgt_hidden; }
+
+dfkv_status check_geom(const dfkv_geom *g) {
+    if (!g) return DFKV_ERR_NULL;
+    if (g->kind != DFKV_GQA && g->kind != DFKV_MLA) return DFKV_ERR_SHAPE;
+    if (g->n_tgt <= 0 || g->tgt_hidden <= 0 || g->hidden <= 0 || g->n_layers <= 0) return DFKV_ERR_SHAPE;
+    if (g->n_layers > DFKV_MAX_LAYERS) return DFKV_ERR_SHAPE;
+    if (g->page_size <= 0 || g->width <= 0 || g->block_size <= 0) return DFKV_ERR_SHAPE;
+    if (!(g->eps >= 0.f) || g->eps > 1.f) return DFKV_ERR_SHAPE;
+    if (k_in(g) % 128 != 0 || g->hidden % 128 != 0 || k_in(g) > (1 << 20) || g->hidden > (1 << 16))
+        return DFKV_ERR_SHAPE;
+    if (g->kind == DFKV_GQA) {
+        if (g->n_kv_heads <= 0 || g->n_kv_heads > 128) return DFKV_ERR_SHAPE;
+        if (g->head_dim != 64 && g->head_dim != 128 && g->head_dim != 256) return DFKV_ERR_SHAPE;
+        if (g->rope_dim != g->head_dim) return DFKV_ERR_SHAPE;
+    } else {
+        if (g->n_kv_heads != 1 || g->head_dim != 0) return DFKV_ERR_SHAPE;
+        if (g->latent_dim <= 0 || g->latent_dim % 64 != 0 || g->latent_dim > 1024) return DFKV_ERR_SHAPE;
+        if (g->rope_dim <= 0 || g->rope_dim % 2 != 0 || g->rope_dim > 128) return DFKV_ERR_SHAPE;
+        if ((g->latent_dim + g->rope_dim) % 64 != 0) return DFKV_ERR_SHAPE;
+    }
+    if (out_dim(g) > (1 << 20)) return DFKV_ERR_SHAPE;
+    return DFKV_OK;
+}
+
+int n_groups(const dfkv_geom *g) { return g->kind == DFKV_GQA ? g->n_layers * g->n_kv_heads : g->n_layers; }
+
+// Split count for the skinny GEMM: S divides the number of 128-wide k-blocks,
+// a split holds at most max_blocks k-blocks (the LDS-staged activation extent),
+// and S is the smallest such count giving kTargetItems work items -- unless that
+// leaves fewer than 4 k-blocks (one per wave) per split while a count with 4 exists.
+int choose_splits(int tiles, int kblocks, int max_blocks) {
+    int first = -1, last_full = -1;
+    for (int S = 1; S <= kblocks; ++S) {
+        if (kblocks % S || kblocks / S > max_blocks) continue;
+        if (kblocks / S >= 4) last_full = S;
+        if ((int64_t)tiles * S >= kTargetItems) {
+            first = S;
+            break;
+        }
+    }
+    if (first < 0) return last_full > 0 ? last_full : kblocks;
+    if (kblocks / first < 4 && last_full > 0) return last_full;
+    return first;
+}
+
+int max_blocks_for(int64_t M) {
+    const int ng = (int)((M + 15) / 16);
+    return ng <= 1 ? 8 : (ng == 2 ? 4 : 2);
+}
+
+struct Plan {
+    int64_t M;
+    bool skinny;
+    int S_fc, S_kv;
+    size_t off_part, off_f, off_g, off_ss, off_tfc, off_tkv, off_tg, total;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+dfkv_status make_plan(const dfkv_geom *g, int32_t n_reqs, Plan *pl) {
+    dfkv_status st = check_geom(g);
+    if (st != DFKV_OK) return st;
+    if (n_reqs < 0) return DFKV_ERR_SHAPE;
+    const int64_t M = (int64_t)n_reqs * g->width;
+    if (M > (1 << 22)) return DFKV_ERR_SHAPE;
+    const int64_t H = g->hidden, O = out_dim(g), K = k_in(g);
+    Plan p{};
+    p.M = M;
+    p.skinny = M <= kSkinnyMaxRows;
+    // Tickets first, at offsets that depend only on the geometry: a workspace
+    // shared by calls of different batch sizes always finds them (zeroed) in the
+    // same place.  The data regions after them need no initialisation.
+    size_t off = 0;
+    p.off_tfc = off; off = up256(off + (size_t)(H / 64) * 4);
+    p.off_tkv = off; off = up256(off + (size_t)(O / 64) * 4);
+    p.off_tg = off;  off = up256(off + (size_t)n_groups(g) * 4);
+    if (p.skinny) {
+        const int Mp = M > 0 ? (int)M : 1;
+        p.S_fc = choose_splits((int)(H / 64), (int)(K / 128), max_blocks_for(M));
+        p.S_kv = choose_splits((int)(O / 64), (int)(H / 128), max_blocks_for(M));
+        const size_t part_elems = (size_t)(p.S_fc * H > p.S_kv * O ? p.S_fc * H : p.S_kv * O) * Mp;
+        p.off_part = off; off = up256(off + part_elems * 4);
+        p.off_f = off;    off = up256(off + (size_t)Mp * H * 2);
+        p.off_ss = off;   off = up256(off + (size_t)(H / 64) * Mp * 4);
+        p.off_g = 0;
+    } else {
+        p.S_fc = p.S_kv = 1;
+        p.off_f = off;    off = up256(off + (size_t)M * H * 2);
+        p.off_g = off;    off = up256(off + (size_t)M * H * 2);
+        p.off_part = p.off_ss = 0;
+    }
+    p.total = off;
+    *pl = p;
+    return DFKV_OK;
+}
+
+NormRopeGeom nr_geom(const dfkv_geom *g, const void *w_knorm, const int32_t *ctx, const float *cs, int32_t cache_len) {
+    NormRopeGeom r{};
+    r.kind = g->kind;
+    r.n_layers = g->n_layers;
+    r.nkv = g->n_kv_heads;
+    r.hd = g->head_dim;
+    r.latent = g->latent_dim;
+    r.rope_dim = g->rope_dim;
+    r.per_layer = per_layer(g);
+    r.width = g->width;
+    r.cache_len = cache_len;
+    r.out_dim = (int32_t)out_dim(g);
+    r.eps = g->eps;
+    r.w_knorm = (const uint16_t *)w_knorm;
+    r.ctx_len_in = ctx;
+    r.cos_sin = cs;
+    return r;
+}
+
+// ----- validation shared by the entry points --------------------------------
+
+dfkv_status check_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t ld,
+                          int32_t n_reqs, const int32_t *ctx, const float *cs, int32_t cache_len, void *kv_out,
+                          uint32_t flags, void *ws, size_t ws_bytes, Plan *pl) {
+    if (!g || !w) return DFKV_ERR_NULL;
+    dfkv_status st = make_plan(g, n_reqs, pl);
+    if (st != DFKV_OK) return st;
+    const bool fuse = (flags & DFKV_FUSE_NORM_ROPE) != 0;
+    if ((flags & ~(uint32_t)DFKV_FUSE_NORM_ROPE) != 0) return DFKV_ERR_SHAPE;
+    if (pl->M == 0) return DFKV_OK;
+    if (!hidden || !kv_out || !w->w_fc || !w->w_hnorm || !w->w_kv || !ws) return DFKV_ERR_NULL;
+    if (fuse && (!w->w_knorm || !ctx || !cs)) return DFKV_ERR_NULL;
+    if (fuse && cache_len <= 0) return DFKV_ERR_SHAPE;
+    const int64_t K = k_in(g), H = g->hidden, O = out_dim(g), M = pl->M;
+    if (ld < K || (ld * 2) % 16 != 0) return DFKV_ERR_LAYOUT;
+    if (!al16(hidden) || !al16(kv_out) || !al16(w->w_fc) || !al16(w->w_hnorm) || !al16(w->w_kv) || !al16(ws))
+        return DFKV_ERR_LAYOUT;
+    if (fuse && (!al4(cs) || ((uintptr_t)w->w_knorm & 1u))) return DFKV_ERR_LAYOUT;
+    if (ws_bytes < pl->total) return DFKV_ERR_WORKSPACE;
+    const size_t kv_bytes = (size_t)M * O * 2;
+    const size_t hid_bytes = (size_t)((M - 1) * ld + K) * 2;
+    if (overlap(kv_out, kv_bytes, hidden, hid_bytes) || overlap(kv_out, kv_bytes, ws, ws_bytes) ||
+        overlap(kv_out, kv_bytes, w->w_fc, (size_t)H * K * 2) || overlap(kv_out, kv_bytes, w->w_kv, (size_t)O * H * 2) ||
+        overlap(kv_out, kv_bytes, w->w_hnorm, (size_t)H * 2) || overlap(ws, ws_bytes, hidden, hid_bytes))
+        return DFKV_ERR_ALIAS;
+    if (fuse) {
+        const size_t kn = (size_t)g->n_layers * (g->kind == DFKV_GQA ? g->head_dim : g->latent_dim) * 2;
+        if (overlap(kv_out, kv_bytes, cs, (size_t)cache_len * g->rope_dim * 4) ||
+            overlap(kv_out, kv_bytes, w->w_knorm, kn) || overlap(kv_out, kv_bytes, ctx, (size_t)n_reqs * 4))
+            return DFKV_ERR_ALIAS;
+    }
+    return DFKV_OK;
+}
+
+dfkv_status check_requests(const dfkv_geom *g, const dfkv_requests *r, bool need_store, bool need_adv) {
+    if (!r) return DFKV_ERR_NULL;
+    if (r->n_reqs < 0) return DFKV_ERR_SHAPE;
+    if (r->n_reqs == 0) return DFKV_OK;
+    if (!r->ctx_len_in || !r->n_acc || !r->alloc_limit || !r->is_dummy) return DFKV_ERR_NULL;
+    if (need_store) {
+        if (!r->block_table) return DFKV_ERR_NULL;
+        if (r->bt_cols <= 0 || r->bt_row_stride < r->bt_cols) return DFKV_ERR_LAYOUT;
+    }
+    if (need_adv) {
+        if (!r->accepted_tokens) return DFKV_ERR_NULL;
+        if (r->acc_stride_req < 0 || r->acc_stride_tok < 0) return DFKV_ERR_LAYOUT;
+    }
+    (void)g;
+    return DFKV_OK;
+}
+
+// Byte extent [lo, hi) of a strided int32 view of n_a x n_b elements.
+size_t extent2(int64_t s_a, int64_t n_a, int64_t s_b, int64_t n_b) {
+    if (n_a <= 0 || n_b <= 0) return 0;
+    return (size_t)(((n_a - 1) * s_a + (n_b - 1) * s_b + 1) * 4);
+}
+
+dfkv_status check_pool(const dfkv_geom *g, const dfkv_pool *pool) {
+    if (!pool) return DFKV_ERR_NULL;
+    if (pool->num_pages < 0) return DFKV_ERR_SHAPE;
+    const int64_t sp = pool->stride_page, ss = pool->stride_slot, sh = pool->stride_head;
+    if (sp <= 0 || ss <= 0 || sp % 8 || ss % 8) return DFKV_ERR_LAYOUT;
+    const int64_t pg = g->page_size;
+    if (g->kind == DFKV_GQA) {
+        const int64_t hd = g->head_dim, nkv = g->n_kv_heads;
+        if (nkv > 1 && (sh <= 0 || sh % 8)) return DFKV_ERR_LAYOUT;
+        const bool nhd = sh >= hd && ss >= nkv * sh;     // [page][slot][head][dim]
+        const bool hnd = ss >= hd && sh >= pg * ss;      // [page][head][slot][dim]
+        if (nkv > 1 ? !(nhd || hnd) : ss < hd) return DFKV_ERR_LAYOUT;
+        const int64_t page_extent = (pg - 1) * ss + (nkv - 1) * (nkv > 1 ? sh : 0) + hd;
+        if (sp < page_extent) return DFKV_ERR_LAYOUT;
+    } else {
+        const int64_t row = g->latent_dim + g->rope_dim;
+        if (ss < row || sp < (pg - 1) * ss + row) return DFKV_ERR_LAYOUT;
+    }
+    for (int l = 0; l < g->n_layers; ++l) {
+        if (!pool->k[l]) return DFKV_ERR_NULL;
+        if (!al16(pool->k[l])) return DFKV_ERR_LAYOUT;
+        if (g->kind == DFKV_GQA) {
+            if (!pool->v[l]) return DFKV_ERR_NULL;
+            if (!al16(pool->v[l])) return DFKV_ERR_LAYOUT;
+        }
+    }
+    return DFKV_OK;
+}
+
+size_t pool_bytes(const dfkv_geom *g, const dfkv_pool *pool) { return (size_t)pool->num_pages * pool->stride_page * 2; }
+
+dfkv_status check_store_outputs(const dfkv_geom *g, const dfkv_requests *r, const dfkv_pool *pool, const void *kv,
+                                const int64_t *slot, const uint8_t *wmask) {
+    const int64_t N = (int64_t)r->n_reqs * g->width;
+    if (N == 0) return DFKV_OK;
+    if (!kv || !slot || !wmask) return DFKV_ERR_NULL;
+    if (!al16(kv) || ((uintptr_t)slot & 7u)) return DFKV_ERR_LAYOUT;
+    const size_t kvb = (size_t)N * out_dim(g) * 2, pb = pool_bytes(g, pool);
+    const void *outs[2] = {slot, wmask};
+    const size_t outb[2] = {(size_t)N * 8, (size_t)N};
+    for (int i = 0; i < 2; ++i) {
+        if (overlap(outs[i], outb[i], kv, kvb)) return DFKV_ERR_ALIAS;
+        for (int l = 0; l < g->n_layers; ++l) {
+            if (overlap(outs[i], outb[i], pool->k[l], pb)) return DFKV_ERR_ALIAS;
+            if (g->kind == DFKV_GQA && overlap(outs[i], outb[i], pool->v[l], pb)) return DFKV_ERR_ALIAS;
+        }
+    }
+    if (overlap(slot, outb[0], wmask, outb[1])) return DFKV_ERR_ALIAS;
+    for (int l = 0; l < g->n_layers; ++l) {
+        if (overlap(kv, kvb, pool->k[l], pb)) return DFKV_ERR_ALIAS;
+        if (g->kind == DFKV_GQA && overlap(kv, kvb, pool->v[l], pb)) return DFKV_ERR_ALIAS;
+    }
+    return DFKV_OK;
+}
+
+dfkv_status check_adv_outputs(const dfkv_geom *g, const dfkv_requests *r, const dfkv_outputs *o) {
+    if (!o) return DFKV_ERR_NULL;
+    const int64_t B = r->n_reqs;
+    if (B == 0) return DFKV_OK;
+    if (!o->c_pos || !o->bonus || !o->emb_ids || !o->q_pos || !o->ctx_len_out || !o->seq_len) return DFKV_ERR_NULL;
+    const int64_t N = B * g->width, bs = g->block_size;
+    const void *outs[6] = {o->c_pos, o->bonus, o->emb_ids, o->q_pos, o->ctx_len_out, o->seq_len};
+    const size_t ob[6] = {(size_t)N * 4, (size_t)B * 4, (size_t)(B * bs) * 4, (size_t)(B * bs) * 4, (size_t)B * 4,
+                          (size_t)B * 4};
+    const void *ins[6] = {r->ctx_len_in, r->n_acc, r->alloc_limit, r->is_dummy, r->accepted_tokens, r->row_valid};
+    const size_t ib[6] = {(size_t)B * 4, (size_t)B * 4, (size_t)B * 4, (size_t)B,
+                          extent2(r->acc_stride_req, B, r->acc_stride_tok, g->width), (size_t)N};
+    for (int i = 0; i < 6; ++i) {
+        for (int j = 0; j < 6; ++j)
+            if (overlap(outs[i], ob[i], ins[j], ib[j])) return DFKV_ERR_ALIAS;
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], ob[i], outs[j], ob[j])) return DFKV_ERR_ALIAS;
+        if (r->block_table && overlap(outs[i], ob[i], r->block_table,
+                                      extent2(r->bt_row_stride, B, 1, r->bt_cols)))
+            return DFKV_ERR_ALIAS;
+    }
+    return DFKV_OK;
+}
+
+StoreParams store_params(const dfkv_geom *g, const void *kv, const dfkv_requests *r, const dfkv_pool *pool,
+                         int64_t *slot, uint8_t *wmask, const dfkv_outputs *o) {
+    StoreParams p;
+    memset(&p, 0, sizeof p);
+    p.kv = (const uint16_t *)kv;
+    p.kv_ld = out_dim(g);
+    p.B = r->n_reqs;
+    p.W = g->width;
+    p.bs_blk = g->block_size;
+    p.pg = g->page_size;
+    p.L = g->n_layers;
+    p.kind = g->kind;
+    p.nkv = g->n_kv_heads;
+    p.hd = g->head_dim;
+    p.per_layer = per_layer(g);
+    p.ctx_len = r->ctx_len_in;
+    p.n_acc = r->n_acc;
+    p.limit = r->alloc_limit;
+    p.dummy = r->is_dummy;
+    p.row_valid = r->row_valid;
+    p.bt = r->block_table;
+    p.bt_stride = r->bt_row_stride;
+    p.bt_cols = r->bt_cols;
+    p.acc = r->accepted_tokens;
+    p.acc_sr = r->acc_stride_req;
+    p.acc_st = r->acc_stride_tok;
+    p.mask_id = r->mask_token_id;
+    if (pool) {
+        p.num_pages = pool->num_pages;
+        for (int l = 0; l < g->n_layers; ++l) {
+            p.pk[l] = (uint16_t *)pool->k[l];
+            p.pv[l] = (uint16_t *)pool->v[l];
+        }
+        p.sp = pool->stride_page;
+        p.ss = pool->stride_slot;
+        p.sh = pool->stride_head;
+    }
+    p.slot = slot;
+    p.wmask = wmask;
+    if (o) {
+        p.c_pos = o->c_pos;
+        p.bonus = o->bonus;
+        p.emb = o->emb_ids;
+        p.q_pos = o->q_pos;
+        p.ctx_out = o->ctx_len_out;
+        p.seq_len = o->seq_len;
+    }
+    return p;
+}
+
+// ----- launches ---------------------------------------------------------------
+
+dfkv_status run_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t ld, int32_t n_reqs,
+                        const int32_t *ctx, const float *cs, int32_t cache_len, void *kv_out, uint32_t flags,
+                        void *ws, const Plan &pl, hipStream_t s) {
+    if (pl.M == 0) return DFKV_OK;
+    const bool fuse = (flags & DFKV_FUSE_NORM_ROPE) != 0;
+    char *wsb = (char *)ws;
+    const int64_t K = k_in(g), H = g->hidden, O = out_dim(g);
+    const NormRopeGeom nr = nr_geom(g, w->w_knorm, ctx, cs, cache_len);
+    hipError_t e;
+    if (pl.skinny) {
+        SkinnyParams p;
+        memset(&p, 0, sizeof p);
+        p.M = (int32_t)pl.M;
+        p.part = (float *)(wsb + pl.off_part);
+        p.nr = nr;
+        // fc: f = bf16(hidden . w_fc^T), plus per-tile sums of squares
+        p.w = (const uint16_t *)w->w_fc;
+        p.x = (const uint16_t *)hidden;
+        p.ldx = ld;
+        p.K = (int32_t)K;
+        p.O = (int32_t)H;
+        p.S = pl.S_fc;
+        p.nb_split = (int32_t)(K / 128 / pl.S_fc);
+        p.ticket = (int32_t *)(wsb + pl.off_tfc);
+        p.f_out = (uint16_t *)(wsb + pl.off_f);
+        p.ss_out = (float *)(wsb + pl.off_ss);
+        if ((e = launch_skinny(p, SK_FC, s)) != hipSuccess) return hip_status(e);
+        // stacked K/V GEMM with hidden_norm applied on load, optional k_norm + RoPE epilogue
+        p.w = (const uint16_t *)w->w_kv;
+        p.x = (const uint16_t *)(wsb + pl.off_f);
+        p.ldx = H;
+        p.K = (int32_t)H;
+        p.O = (int32_t)O;
+        p.S = pl.S_kv;
+        p.nb_split = (int32_t)(H / 128 / pl.S_kv);
+        p.ticket = (int32_t *)(wsb + pl.off_tkv);
+        p.w_hn = (const uint16_t *)w->w_hnorm;
+        p.ss_in = (const float *)(wsb + pl.off_ss);
+        p.kv_out = (uint16_t *)kv_out;
+        p.gticket = (int32_t *)(wsb + pl.off_tg);
+        p.fuse = fuse ? 1 : 0;
+        if ((e = launch_skinny(p, SK_KV, s)) != hipSuccess) return hip_status(e);
+        return DFKV_OK;
+    }
+    uint16_t *f = (uint16_t *)(wsb + pl.off_f), *gb = (uint16_t *)(wsb + pl.off_g);
+    TiledParams t{(const uint16_t *)hidden, ld, (const uint16_t *)w->w_fc, f, H, (int32_t)pl.M, (int32_t)K, (int32_t)H};
+    if ((e = launch_tiled(t, s)) != hipSuccess) return hip_status(e);
+    if ((e = launch_hidden_norm(f, (const uint16_t *)w->w_hnorm, gb, (int)pl.M, (int)H, g->eps, s)) != hipSuccess)
+        return hip_status(e);
+    TiledParams t2{gb, H, (const uint16_t *)w->w_kv, (uint16_t *)kv_out, O, (int32_t)pl.M, (int32_t)H, (int32_t)O};
+    if ((e = launch_tiled(t2, s)) != hipSuccess) return hip_status(e);
+    if (fuse && (e = launch_norm_rope(nr, (uint16_t *)kv_out, (int)pl.M, s)) != hipSuccess) return hip_status(e);
+    return DFKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dfkv_status_string(dfkv_status s) {
+    switch (s) {
+        case DFKV_OK: return "DFKV_OK";
+        case DFKV_ERR_NULL: return "DFKV_ERR_NULL: a required pointer is NULL";
+        case DFKV_ERR_SHAPE: return "DFKV_ERR_SHAPE: unsupported or inconsistent sizes";
+        case DFKV_ERR_LAYOUT: return "DFKV_ERR_LAYOUT: misaligned pointer or bad stride";
+        case DFKV_ERR_ALIAS: return "DFKV_ERR_ALIAS: an output overlaps an input";
+        case DFKV_ERR_WORKSPACE: return "DFKV_ERR_WORKSPACE: workspace too small";
+        case DFKV_ERR_HIP: return "DFKV_ERR_HIP: kernel launch failed";
+    }
+    return "unknown dfkv_status";
+}
+
+const char *dfkv_version(void) { return "libdfkv 0.1 (gfx950)"; }
+
+const char *dfkv_hip_error_string(void) { return hipGetErrorString(g_last_hip_error); }
+
+dfkv_status dfkv_workspace_size(const dfkv_geom *g, int32_t n_reqs, size_t *bytes) {
+    if (!g || !bytes) return DFKV_ERR_NULL;
+    Plan pl;
+    dfkv_status st = make_plan(g, n_reqs, &pl);
+    if (st != DFKV_OK) return st;
+    *bytes = pl.total;
+    return DFKV_OK;
+}
+
+dfkv_status dfkv_workspace_init(void *ws, size_t ws_bytes, dfkv_stream_t stream) {
+    if (!ws) return DFKV_ERR_NULL;
+    if (!al16(ws)) return DFKV_ERR_LAYOUT;
+    return hip_status(launch_fill_zero(ws, ws_bytes, (hipStream_t)stream));
+}
+
+dfkv_status dfkv_rope_cache_build(const dfkv_rope *rope, float *cos_sin, int32_t cache_len, dfkv_stream_t stream) {
+    if (!rope || !cos_sin) return DFKV_ERR_NULL;
+    if (rope->rot <= 0 || rope->rot % 2 || rope->rot > 1024 || cache_len <= 0) return DFKV_ERR_SHAPE;
+    if (!(rope->theta > 1.0)) return DFKV_ERR_SHAPE;
+    if (rope->yarn && (!(rope->factor > 0.0) || !(rope->orig_ctx > 0.0) || !(rope->beta_fast > 0.0) ||
+                       !(rope->beta_slow > 0.0)))
+        return DFKV_ERR_SHAPE;
+    if (!al4(cos_sin)) return DFKV_ERR_LAYOUT;
+    return hip_status(launch_rope_cache(*rope, cos_sin, cache_len, (hipStream_t)stream));
+}
+
+dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t hidden_row_stride,
+                         int32_t n_reqs, const int32_t *ctx_len_in, const float *cos_sin, int32_t cache_len,
+                         void *kv_out, uint32_t flags, void *ws, size_t ws_bytes, dfkv_stream_t stream) {
+    Plan pl;
+    dfkv_status st = check_project(g, w, hidden, hidden_row_stride, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out,
+                                   flags, ws, ws_bytes, &pl);
+    if (st != DFKV_OK) return st;
+    return run_project(g, w, hidden, hidden_row_stride, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out, flags, ws, pl,
+                       (hipStream_t)stream);
+}
+
+dfkv_status dfkv_norm_rope(const dfkv_geom *g, const void *w_knorm, int32_t n_reqs, const int32_t *ctx_len_in,
+                           const float *cos_sin, int32_t cache_len, void *kv, dfkv_stream_t stream) {
+    dfkv_status st = check_geom(g);
+    if (st != DFKV_OK) return st;
+    if (n_reqs < 0 || cache_len <= 0) return DFKV_ERR_SHAPE;
+    const int64_t N = (int64_t)n_reqs * g->width;
+    if (N == 0) return DFKV_OK;
+    if (!w_knorm || !ctx_len_in || !cos_sin || !kv) return DFKV_ERR_NULL;
+    if (!al16(kv) || !al4(cos_sin) || ((uintptr_t)w_knorm & 1u)) return DFKV_ERR_LAYOUT;
+    const size_t kvb = (size_t)N * out_dim(g) * 2;
+    const size_t kn = (size_t)g->n_layers * (g->kind == DFKV_GQA ? g->head_dim : g->latent_dim) * 2;
+    if (overlap(kv, kvb, cos_sin, (size_t)cache_len * g->rope_dim * 4) || overlap(kv, kvb, w_knorm, kn) ||
+        overlap(kv, kvb, ctx_len_in, (size_t)n_reqs * 4))
+        return DFKV_ERR_ALIAS;
+    const NormRopeGeom nr = nr_geom(g, w_knorm, ctx_len_in, cos_sin, cache_len);
+    return hip_status(launch_norm_rope(nr, (uint16_t *)kv, (int)N, (hipStream_t)stream));
+}
+
+dfkv_status dfkv_paged_store(const dfkv_geom *g, const void *kv, const dfkv_requests *req, const dfkv_pool *pool,
+                             int64_t *slot_out, uint8_t *write_mask_out, dfkv_stream_t stream) {
+    dfkv_status st = check_geom(g);
+    if (st != DFKV_OK) return st;
+    if ((st = check_requests(g, req, true, false)) != DFKV_OK) return st;
+    if (req->n_reqs == 0) return DFKV_OK;
+    if ((st = check_pool(g, pool)) != DFKV_OK) return st;
+    if ((st = check_store_outputs(g, req, pool, kv, slot_out, write_mask_out)) != DFKV_OK) return st;
+    const StoreParams p = store_params(g, kv, req, pool, slot_out, write_mask_out, nullptr);
+    return hip_status(launch_store_advance(p, true, false, (hipStream_t)stream));
+}
+
+dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfkv_outputs *out, dfkv_stream_t stream) {
+    dfkv_status st = check_geom(g);
+    if (st != DFKV_OK) return st;
+    if ((st = check_requests(g, req, false, true)) != DFKV_OK) return st;
+    if (req->n_reqs == 0) return DFKV_OK;
+    if ((st = check_adv_outputs(g, req, out)) != DFKV_OK) return st;
+    const StoreParams p = store_params(g, nullptr, req, nullptr, nullptr, nullptr, out);
+    return hip_status(launch_store_advance(p, false, true, (hipStream_t)stream));
+}
+
+static dfkv_status check_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
+                                       const dfkv_pool *pool, const dfkv_outputs *out) {
+    dfkv_status st = check_geom(g);
+    if (st != DFKV_OK) return st;
+    if ((st = check_requests(g, req, true, true)) != DFKV_OK) return st;
+    if (req->n_reqs == 0) return DFKV_OK;
+    if (!out) return DFKV_ERR_NULL;
+    if ((st = check_pool(g, pool)) != DFKV_OK) return st;
+    if ((st = check_store_outputs(g, req, pool, kv, out->slot, out->write_mask)) != DFKV_OK) return st;
+    if ((st = check_adv_outputs(g, req, out)) != DFKV_OK) return st;
+    const int64_t N = (int64_t)req->n_reqs * g->width;
+    const size_t pb = pool_bytes(g, pool);
+    const void *outs[6] = {out->c_pos, out->bonus, out->emb_ids, out->q_pos, out->ctx_len_out, out->seq_len};
+    const size_t ob[6] = {(size_t)N * 4, (size_t)req->n_reqs * 4, (size_t)req->n_reqs * g->block_size * 4,
+                          (size_t)req->n_reqs * g->block_size * 4, (size_t)req->n_reqs * 4, (size_t)req->n_reqs * 4};
+    for (int i = 0; i < 6; ++i) {
+        if (overlap(outs[i], ob[i], kv, (size_t)N * out_dim(g) * 2) || overlap(outs[i], ob[i], out->slot, (size_t)N * 8) ||
+            overlap(outs[i], ob[i], out->write_mask, (size_t)N))
+            return DFKV_ERR_ALIAS;
+        for (int l = 0; l < g->n_layers; ++l) {
+            if (overlap(outs[i], ob[i], pool->k[l], pb)) return DFKV_ERR_ALIAS;
+            if (g->kind == DFKV_GQA && overlap(outs[i], ob[i], pool->v[l], pb)) return DFKV_ERR_ALIAS;
+        }
+    }
+    return DFKV_OK;
+}
+
+dfkv_status dfkv_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req, const dfkv_pool *pool,
+                               const dfkv_outputs *out, dfkv_stream_t stream) {
+    dfkv_status st = check_store_advance(g, kv, req, pool, out);
+    if (st != DFKV_OK) return st;
+    if (req->n_reqs == 0) return DFKV_OK;
+    const StoreParams p = store_params(g, kv, req, pool, out->slot, out->write_mask, out);
+    return hip_status(launch_store_advance(p, true, true, (hipStream_t)stream));
+}
+
+dfkv_status dfkv_step(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t hidden_row_stride,
+                      const dfkv_requests *req, const float *cos_sin, int32_t cache_len, void *kv_out,
+                      const dfkv_pool *pool, const dfkv_outputs *out, void *ws, size_t ws_bytes, dfkv_stream_t stream) {
+    if (!req) return DFKV_ERR_NULL;
+    Plan pl;
+    dfkv_status st = check_project(g, w, hidden, hidden_row_stride, req->n_reqs, req->ctx_len_in, cos_sin, cache_len,
+                                   kv_out, DFKV_FUSE_NORM_ROPE, ws, ws_bytes, &pl);
+    if (st != DFKV_OK) return st;
+    if ((st = check_store_advance(g, kv_out, req, pool, out)) != DFKV_OK) return st;
+    if (req->n_reqs == 0) return DFKV_OK;
+    // the bookkeeping outputs must not land in the projection's inputs or workspace either
+    const int64_t N = (int64_t)req->n_reqs * g->width;
+    const void *outs[8] = {out->slot, out->write_mask, out->c_pos, out->bonus, out->emb_ids, out->q_pos,
+                           out->ctx_len_out, out->seq_len};
+    const size_t ob[8] = {(size_t)N * 8, (size_t)N, (size_t)N * 4, (size_t)req->n_reqs * 4,
+                          (size_t)req->n_reqs * g->block_size * 4, (size_t)req->n_reqs * g->block_size * 4,
+                          (size_t)req->n_reqs * 4, (size_t)req->n_reqs * 4};
+    const size_t hid_bytes = (size_t)((N - 1) * hidden_row_stride + k_in(g)) * 2;
+    for (int i = 0; i < 8; ++i)
+        if (overlap(outs[i], ob[i], ws, ws_bytes) || overlap(outs[i], ob[i], hidden, hid_bytes) ||
+            overlap(outs[i], ob[i], cos_sin, (size_t)cache_len * g->rope_dim * 4))
+            return DFKV_ERR_ALIAS;
+    st = run_project(g, w, hidden, hidden_row_stride, req->n_reqs, req->ctx_len_in, cos_sin, cache_len, kv_out,
+                     DFKV_FUSE_NORM_ROPE, ws, pl, (hipStream_t)stream);
+    if (st != DFKV_OK) return st;
+    const StoreParams p = store_params(g, kv_out, req, pool, out->slot, out->write_mask, out);
+    return hip_status(launch_store_advance(p, true, true, (hipStream_t)stream));
+}
+
+}  // extern "C"

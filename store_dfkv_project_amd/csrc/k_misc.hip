@@ -1,0 +1,178 @@
+// k_misc.hip -- standalone k_norm/RoPE, hidden_norm, the cos/sin cache builder
+// and a zero-fill kernel.
+#include <math.h>
+
+#include "dfkv_internal.hpp"
+
+namespace dfkv {
+
+// ---------------------------------------------------------------------------
+// k_norm (or latent norm) + RoPE in place (TensorRT-LLM PR #13995, commits
+// "fuse cross-layer k_norm" and "match RoPE between context and query for
+// YaRN").  One wave per (row, layer, K head) for GQA, per (row, layer) for MLA.
+// ---------------------------------------------------------------------------
+struct NormRopeArgs {
+    NormRopeGeom g;
+    uint16_t *kv;
+    int n_rows;
+};
+
+__global__ __launch_bounds__(256) void k_norm_rope(const NormRopeArgs a) {
+    const NormRopeGeom &g = a.g;
+    uint16_t *kv = a.kv;
+    const int n_rows = a.n_rows;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wv = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (g.kind == DFKV_GQA) {
+        const int64_t per_row = (int64_t)g.n_layers * g.nkv;
+        if (wv >= (int64_t)n_rows * per_row) return;
+        const int row = (int)(wv / per_row);
+        const int rem = (int)(wv - row * per_row);
+        const int l = rem / g.nkv, h = rem - l * g.nkv;
+        norm_rope_gqa_head(g, kv + (int64_t)row * g.out_dim + (int64_t)l * g.per_layer + h * g.hd, l, row, lane);
+    } else {
+        if (wv >= (int64_t)n_rows * g.n_layers) return;
+        const int row = (int)(wv / g.n_layers);
+        const int l = (int)(wv - (int64_t)row * g.n_layers);
+        norm_rope_mla_layer(g, kv + (int64_t)row * g.out_dim + (int64_t)l * g.per_layer, l, row, lane);
+    }
+}
+
+hipError_t launch_norm_rope(const NormRopeGeom &g, uint16_t *kv, int n_rows, hipStream_t s) {
+    const int64_t waves = (int64_t)n_rows * g.n_layers * (g.kind == DFKV_GQA ? g.nkv : 1);
+    if (waves == 0) return hipSuccess;
+    const int64_t blocks = (waves + 3) / 4;
+    return launch1(k_norm_rope, dim3((unsigned)blocks), dim3(256), s, NormRopeArgs{g, kv, n_rows});
+}
+
+// ---------------------------------------------------------------------------
+// hidden_norm: g[n][:] = bf16(w * f[n][:] / sqrt(mean(f[n]^2) + eps)); one
+// workgroup per row (used by the large-batch path; the small-batch path folds
+// it into the stacked GEMM's operand load).
+// ---------------------------------------------------------------------------
+struct HiddenNormArgs {
+    const uint16_t *f, *w;
+    uint16_t *g;
+    int H;
+    float eps;
+};
+
+__global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
+    const uint16_t *f = a.f, *w = a.w;
+    uint16_t *g = a.g;
+    const int H = a.H;
+    const float eps = a.eps;
+    const int row = blockIdx.x;
+    const uint16_t *x = f + (int64_t)row * H;
+    __shared__ float red[4];
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < (H >> 3); c += blockDim.x) {
+        const u32x4 v = *(const u32x4 *)(x + (c << 3));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            float a = bf_lo(v[q]), b = bf_hi(v[q]);
+            ss += a * a + b * b;
+        }
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = red[0] + red[1] + red[2] + red[3];
+    const float rinv = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int c = threadIdx.x; c < (H >> 3); c += blockDim.x) {
+        const u32x4 v = *(const u32x4 *)(x + (c << 3));
+        const u32x4 wv = *(const u32x4 *)(w + (c << 3));
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            o[q] = pack2(bf_lo(wv[q]) * (bf_lo(v[q]) * rinv), bf_hi(wv[q]) * (bf_hi(v[q]) * rinv));
+        *(u32x4 *)(g + (int64_t)row * H + (c << 3)) = o;
+    }
+}
+
+hipError_t launch_hidden_norm(const uint16_t *f, const uint16_t *w, uint16_t *g, int n_rows, int H, float eps,
+                              hipStream_t s) {
+    if (n_rows == 0) return hipSuccess;
+    return launch1(k_hidden_norm, dim3(n_rows), dim3(256), s, HiddenNormArgs{f, w, g, H, eps});
+}
+
+// ---------------------------------------------------------------------------
+// cos/sin cache in fp64 (stored fp32).  Plain RoPE: inv_i = theta^(-2i/rot).
+// YaRN (Peng et al. 2023, "NTK-by-parts" + attention temperature, in the HF
+// formulation that honours truncate=false): the correction dim for n turns is
+// rot*ln(orig_ctx/(2*pi*n)) / (2 ln theta); lo from beta_fast, hi from
+// beta_slow, clamped to [0, rot-1] (floor/ceil first only if truncate); a
+// linear ramp over i in [lo, hi] moves inv_i from the original value to
+// inv_i/factor; cos and sin are scaled by 0.1*ln(factor) + 1.
+// One thread per (position, pair index).
+// ---------------------------------------------------------------------------
+struct RopeCacheArgs {
+    dfkv_rope r;
+    float *cs;
+    int cache_len;
+};
+
+__global__ __launch_bounds__(256) void k_rope_cache(const RopeCacheArgs args) {
+    const dfkv_rope &r = args.r;
+    float *cs = args.cs;
+    const int cache_len = args.cache_len;
+    const int half = r.rot >> 1;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= (int64_t)cache_len * half) return;
+    const int p = (int)(t / half);
+    const int i = (int)(t - (int64_t)p * half);
+    double inv = pow(r.theta, -(2.0 * i) / (double)r.rot);
+    double m = 1.0;
+    if (r.yarn) {
+        const double two_pi = 6.283185307179586476925286766559;
+        const double denom = 2.0 * log(r.theta);
+        double lo = (double)r.rot * log(r.orig_ctx / (r.beta_fast * two_pi)) / denom;
+        double hi = (double)r.rot * log(r.orig_ctx / (r.beta_slow * two_pi)) / denom;
+        if (r.truncate) {
+            lo = floor(lo);
+            hi = ceil(hi);
+        }
+        lo = lo < 0.0 ? 0.0 : lo;
+        hi = hi > (double)(r.rot - 1) ? (double)(r.rot - 1) : hi;
+        if (lo == hi) hi += 0.001;
+        double ramp = ((double)i - lo) / (hi - lo);
+        ramp = ramp < 0.0 ? 0.0 : (ramp > 1.0 ? 1.0 : ramp);
+        inv = (inv / r.factor) * ramp + inv * (1.0 - ramp);
+        if (r.factor > 1.0) m = 0.1 * log(r.factor) + 1.0;
+    }
+    const double a = (double)p * inv;
+    cs[(int64_t)p * r.rot + i] = (float)(cos(a) * m);
+    cs[(int64_t)p * r.rot + half + i] = (float)(sin(a) * m);
+}
+
+hipError_t launch_rope_cache(const dfkv_rope &r, float *cs, int cache_len, hipStream_t s) {
+    const int64_t n = (int64_t)cache_len * (r.rot / 2);
+    if (n == 0) return hipSuccess;
+    return launch1(k_rope_cache, dim3((unsigned)((n + 255) / 256)), dim3(256), s, RopeCacheArgs{r, cs, cache_len});
+}
+
+// ---------------------------------------------------------------------------
+// Zero-fill with vector stores (used to prepare a workspace; a kernel rather
+// than a memset node so that it can sit inside a captured graph).
+// ---------------------------------------------------------------------------
+struct FillArgs {
+    uint32_t *p;
+    size_t n_words;
+};
+
+__global__ __launch_bounds__(256) void k_fill_zero(const FillArgs a) {
+    uint32_t *p = a.p;
+    const size_t n_words = a.n_words;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n_words; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+    const size_t words = bytes / 4;
+    if (words == 0) return hipSuccess;
+    size_t blocks = (words + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    return launch1(k_fill_zero, dim3((unsigned)blocks), dim3(256), s, FillArgs{(uint32_t *)p, words});
+}
+
+}  // namespace dfkv

@@ -1,0 +1,166 @@
+"""Projection kernels on the GPU against the oracle: cos/sin cache, k_norm/RoPE,
+and the fc -> hidden_norm -> stacked GEMM -> k_norm/RoPE projection on both the
+small-batch (split-K weight streaming) and the large-batch (tiled) paths, with
+ragged row counts.  K/V within |d| <= 2e-2 + 1e-2*|ref|."""
+import numpy as np
+import pytest
+
+from dfkv_workloads import GQA, MLA, Geometry, RopeSpec, Workload, bf16_bits, make_weights, MASK_TOKEN_ID
+from gpu_helpers import assert_close_bf16, small_geom
+
+pytestmark = pytest.mark.gpu
+
+ROPES = [
+    ("plain-64", RopeSpec(theta=1e6, rot=64), 200),
+    ("plain-128", RopeSpec(theta=1e6, rot=128), 40000),
+    ("yarn40-64", RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0), 393216 + 32),
+    ("yarn4-128", RopeSpec(theta=1e6, rot=128, yarn=True, factor=4.0, orig_ctx=32768.0), 65536 + 40),
+    ("yarn40-64-trunc", RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0, truncate=True), 5000),
+    ("plain-16-1e4", RopeSpec(theta=1e4, rot=16), 3000),
+]
+
+
+@pytest.mark.parametrize("name,rope,cache_len", ROPES, ids=[r[0] for r in ROPES])
+def test_rope_cache_matches_oracle(orc, name, rope, cache_len):
+    """Both caches take fp64 angles; they may differ only by fp32 rounding of nearly equal doubles."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    from store_dfkv_project_amd.step import rope_struct
+    cs = torch.empty((cache_len, rope.rot), dtype=torch.float32, device="cuda")
+    dfkv.dfkv_rope_cache_build(rope_struct(rope), cs)
+    got = cs.cpu().numpy()
+    want = orc.rope_cache(rope, cache_len)
+    diff = np.abs(got.astype(np.float64) - want.astype(np.float64))
+    ulp = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+    bad = diff > np.maximum(ulp, 1e-9)
+    assert not bad.any(), f"{int(bad.sum())} entries differ; max diff {diff.max()}"
+
+
+def _proj_workload(geom: Geometry, B: int, seed: int, rope: RopeSpec, cache_len: int, ctx_hi: int) -> Workload:
+    rng = np.random.default_rng(seed)
+    W = geom.width
+    N = B * W
+    hidden = np.full((N, geom.k_in + 8), 0x7FC0, np.uint16)      # NaN padding past k_in: never read
+    hidden[:, :geom.k_in] = bf16_bits(rng.standard_normal((N, geom.k_in)).astype(np.float32))
+    w = make_weights(geom, rng)
+    ctx = rng.integers(0, ctx_hi, size=B).astype(np.int32)
+    ctx[0] = 0                                                   # position 0: rotation is the identity
+    if B > 2:
+        ctx[1] = cache_len + 5                                   # past the cache: clamped to its last row
+    return Workload(config_id=-1, name="proj", geom=geom, rope=rope, n_reqs=B, hidden=hidden,
+                    hidden_row_stride=geom.k_in + 8, w_fc=w["w_fc"], w_hnorm=w["w_hnorm"], w_kv=w["w_kv"],
+                    w_knorm=w["w_knorm"], ctx_len=ctx, n_acc=np.full(B, W, np.int32),
+                    alloc_limit=np.full(B, 1 << 30, np.int32), is_dummy=np.zeros(B, np.uint8), row_valid=None,
+                    block_table=np.zeros((B, 1), np.int32), accepted_tokens=np.zeros((B, W), np.int32),
+                    acc_stride_req=W, acc_stride_tok=1, mask_token_id=MASK_TOKEN_ID, num_pages=1,
+                    cache_len=cache_len)
+
+
+GQA_G = Geometry(kind=GQA, n_tgt=2, tgt_hidden=256, hidden=384, n_layers=2, n_kv_heads=2, head_dim=128, latent_dim=0,
+                 rope_dim=128, eps=1e-6, page_size=16, width=4, block_size=4)
+GQA_G64 = Geometry(kind=GQA, n_tgt=3, tgt_hidden=256, hidden=256, n_layers=2, n_kv_heads=2, head_dim=64, latent_dim=0,
+                   rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
+GQA_G256 = Geometry(kind=GQA, n_tgt=1, tgt_hidden=640, hidden=512, n_layers=1, n_kv_heads=3, head_dim=256,
+                    latent_dim=0, rope_dim=256, eps=1e-6, page_size=16, width=3, block_size=4)
+MLA_G = Geometry(kind=MLA, n_tgt=2, tgt_hidden=256, hidden=512, n_layers=2, n_kv_heads=1, head_dim=0, latent_dim=512,
+                 rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=7)
+
+PROJ_CASES = [
+    # name, geom, B, rope
+    ("gqa128-B1", GQA_G, 1, RopeSpec(theta=1e6, rot=128)),
+    ("gqa128-B5", GQA_G, 5, RopeSpec(theta=1e6, rot=128, yarn=True, factor=4.0, orig_ctx=1024.0)),
+    ("gqa128-B9-ng3", GQA_G, 9, RopeSpec(theta=1e6, rot=128)),
+    ("gqa128-B16-ng4", GQA_G, 16, RopeSpec(theta=1e6, rot=128)),
+    ("gqa128-B17-tiled", GQA_G, 17, RopeSpec(theta=1e6, rot=128)),
+    ("gqa128-B40-tiled", GQA_G, 40, RopeSpec(theta=1e6, rot=128, yarn=True, factor=4.0, orig_ctx=1024.0)),
+    ("gqa64-B2", GQA_G64, 2, RopeSpec(theta=1e6, rot=64)),
+    ("gqa64-B37-tiled", GQA_G64, 37, RopeSpec(theta=1e6, rot=64)),
+    ("gqa256-B3", GQA_G256, 3, RopeSpec(theta=1e4, rot=256)),
+    ("gqa256-B30-tiled", GQA_G256, 30, RopeSpec(theta=1e4, rot=256)),
+    ("mla-B1", MLA_G, 1, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
+    ("mla-B3", MLA_G, 3, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
+    ("mla-B33-tiled", MLA_G, 33, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
+]
+
+
+def _run_case(orc, name, geom, B, rope, seed=7):
+    import torch
+    from store_dfkv_project_amd import dfkv
+    from store_dfkv_project_amd.step import DeviceStep
+    wl = _proj_workload(geom, B, seed, rope, cache_len=3000, ctx_hi=2900)
+    ds = DeviceStep(wl)
+    cs = orc.rope_cache(rope, wl.cache_len)
+    ref = orc.project(geom, wl.hidden, wl.w_fc, wl.w_hnorm, wl.w_kv, wl.w_knorm, wl.ctx_len, cs)
+    return wl, ds, ref
+
+
+@pytest.mark.parametrize("name,geom,B,rope", PROJ_CASES, ids=[c[0] for c in PROJ_CASES])
+def test_project_matches_oracle(orc, name, geom, B, rope):
+    import torch
+    from store_dfkv_project_amd import dfkv
+    wl, ds, ref = _run_case(orc, name, geom, B, rope)
+    # unfused: kv_out = y (stacked GEMM output before k_norm / RoPE)
+    ds.kv_out.fill_(0x7FC0)
+    ds.project(flags=0)
+    torch.cuda.synchronize()
+    assert_close_bf16(ds.bits(ds.kv_out), ref["y"], f"{name} y")
+    # standalone k_norm + RoPE on the GPU's y
+    y_gpu = ds.kv_out.clone()
+    ds.norm_rope(y_gpu)
+    torch.cuda.synchronize()
+    want_nr = orc.norm_rope(geom, ds.bits(ds.kv_out), wl.w_knorm, wl.ctx_len, orc.rope_cache(rope, wl.cache_len))
+    assert_close_bf16(ds.bits(y_gpu), want_nr, f"{name} norm_rope")
+    # fused
+    ds.kv_out.fill_(0x7FC0)
+    ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    stats = assert_close_bf16(ds.bits(ds.kv_out), ref["kv"], f"{name} kv")
+    # deterministic: a second call gives the same bits
+    first = ds.kv_out.clone()
+    ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    assert torch.equal(first, ds.kv_out), "projection is not deterministic"
+
+
+def test_workspace_shared_across_batch_sizes(orc):
+    """One workspace (sized for the largest call) serves alternating batch sizes: tickets self-reset."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    from store_dfkv_project_amd.step import DeviceStep, geom_struct
+    rope = RopeSpec(theta=1e6, rot=128)
+    cases = []
+    for B in (1, 16, 3, 40, 1):
+        wl = _proj_workload(GQA_G, B, 100 + B, rope, cache_len=3000, ctx_hi=2900)
+        cases.append(wl)
+    need = max(dfkv.dfkv_workspace_size(geom_struct(GQA_G), wl.n_reqs) for wl in cases)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    dfkv.dfkv_workspace_init(ws, need)
+    cs_o = orc.rope_cache(rope, 3000)
+    for wl in cases:
+        ds = DeviceStep(wl)
+        ds.ws, ds.ws_bytes = ws, need
+        ds.project()
+        torch.cuda.synchronize()
+        ref = orc.project(GQA_G, wl.hidden, wl.w_fc, wl.w_hnorm, wl.w_kv, wl.w_knorm, wl.ctx_len, cs_o)
+        assert_close_bf16(ds.bits(ds.kv_out), ref["kv"], f"B={wl.n_reqs}")
+
+
+@pytest.mark.parametrize("kind", [GQA, MLA])
+def test_norm_rope_far_positions(orc, kind):
+    """k_norm + RoPE with YaRN at positions up to 393k, on random y."""
+    import torch
+    from store_dfkv_project_amd.step import DeviceStep
+    geom = GQA_G if kind == GQA else MLA_G
+    rope = (RopeSpec(theta=1e6, rot=128, yarn=True, factor=4.0, orig_ctx=32768.0) if kind == GQA else
+            RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0))
+    wl = _proj_workload(geom, 6, 3, rope, cache_len=393216 + 64, ctx_hi=393216)
+    wl.ctx_len[:] = [0, 393216, 131072, 2048, 65530, 393216 + 63]
+    ds = DeviceStep(wl)
+    rng = np.random.default_rng(5)
+    y = bf16_bits((rng.standard_normal((ds.N, geom.out_dim)) * 2).astype(np.float32))
+    ds.kv_out.copy_(torch.from_numpy(y.view(np.int16)).cuda())
+    ds.ctx_len.copy_(torch.from_numpy(wl.ctx_len).cuda())
+    ds.norm_rope(ds.kv_out)
+    torch.cuda.synchronize()
+    want = orc.norm_rope(geom, y, wl.w_knorm, wl.ctx_len, orc.rope_cache(rope, wl.cache_len))
+    assert_close_bf16(ds.bits(ds.kv_out), want, "norm_rope far positions")
