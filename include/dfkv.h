@@ -211,11 +211,11 @@ const char *dfkv_hip_error_string(void);
  * Errors: NULL if g or bytes is NULL; SHAPE for an unsupported geometry. */
 dfkv_status dfkv_workspace_size(const dfkv_geom *g, int32_t n_reqs, size_t *bytes);
 
-/* Prepare a workspace once after allocating it (zeroes it with a kernel, not a
- * memset).  The workspace starts with the split-K tile tickets, at offsets that
- * depend only on the geometry; every dfkv_project / dfkv_step leaves them zeroed
- * again, so one workspace sized for the largest batch serves every batch size.
- * Two calls that share one workspace must not run concurrently.
+/* Zero-fill a workspace with a kernel (not a memset, so it may sit in a captured
+ * graph).  Optional: the workspace carries no state from one call to the next
+ * (it holds the call's intermediates: f and its statistics, the K/V GEMM's
+ * partial sums), so one workspace sized for the largest batch serves every batch
+ * size.  Two calls that share one workspace must not run concurrently.
  * Errors: NULL; LAYOUT (not 16-byte aligned); HIP. */
 dfkv_status dfkv_workspace_init(void *ws, size_t ws_bytes, dfkv_stream_t stream);
 
@@ -245,12 +245,29 @@ dfkv_status dfkv_rope_cache_build(const dfkv_rope *rope, float *cos_sin, int32_t
  *  kv_out: bf16 [N][O] contiguous, 16-byte aligned; must not overlap hidden,
  *          the weights, cos_sin or ws.
  *  cos_sin/cache_len: needed only with DFKV_FUSE_NORM_ROPE.
- *  ws: >= dfkv_workspace_size bytes, prepared by dfkv_workspace_init.
+ *  ws: >= dfkv_workspace_size bytes of device memory.
  * Errors: NULL, SHAPE, LAYOUT, ALIAS, WORKSPACE, HIP. */
 dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
                          int64_t hidden_row_stride, int32_t n_reqs, const int32_t *ctx_len_in,
                          const float *cos_sin, int32_t cache_len, void *kv_out, uint32_t flags,
                          void *ws, size_t ws_bytes, dfkv_stream_t stream);
+
+/* The two stages of dfkv_project, for callers that want to place them apart
+ * (dfkv_project == dfkv_project_fc then dfkv_project_kv on the same stream and
+ * workspace).
+ * dfkv_project_fc: f = bf16(hidden . w_fc^T) and what hidden_norm needs of it
+ *   (its row statistics and w_hnorm-weighted copy, or the normalised rows) into
+ *   ws.  Reads hidden, w_fc and w_hnorm only.
+ * dfkv_project_kv: from what dfkv_project_fc left in ws (same geometry and
+ *   n_reqs): hidden_norm, the stacked GEMM and, with DFKV_FUSE_NORM_ROPE,
+ *   k_norm + RoPE into kv_out.
+ * Arguments, layouts and errors as dfkv_project. */
+dfkv_status dfkv_project_fc(const dfkv_geom *g, const void *w_fc, const void *w_hnorm, const void *hidden,
+                            int64_t hidden_row_stride, int32_t n_reqs, void *ws, size_t ws_bytes,
+                            dfkv_stream_t stream);
+dfkv_status dfkv_project_kv(const dfkv_geom *g, const dfkv_weights *w, int32_t n_reqs, const int32_t *ctx_len_in,
+                            const float *cos_sin, int32_t cache_len, void *kv_out, uint32_t flags, void *ws,
+                            size_t ws_bytes, dfkv_stream_t stream);
 
 /* k_norm (or latent norm) and RoPE in place on a stacked projection y.
  * GQA, every K head (l, h) of every row: u = bf16(w_knorm[l] * y / sqrt(mean(y^2)+eps)),

@@ -18,7 +18,7 @@ dfkv_status hip_status(hipError_t e) {
 }
 
 constexpr int kSkinnyMaxRows = 64;   // M = B*W handled by the weight-streaming split-K path
-constexpr int kTargetItems = 768;    // split-K work items aimed for per GEMM (256 CUs x 3)
+constexpr int kTargetItems = 512;    // K/V GEMM workgroups aimed for (256 CUs x 2)
 
 bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool al4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
@@ -58,37 +58,29 @@ dfkv_status check_geom(const dfkv_geom *g) {
     return DFKV_OK;
 }
 
-int n_groups(const dfkv_geom *g) { return g->kind == DFKV_GQA ? g->n_layers * g->n_kv_heads : g->n_layers; }
-
-// Split count for the skinny GEMM: S divides the number of 128-wide k-blocks,
-// a split holds at most max_blocks k-blocks (the LDS-staged activation extent),
-// and S is the smallest such count giving kTargetItems work items -- unless that
-// leaves fewer than 4 k-blocks (one per wave) per split while a count with 4 exists.
-int choose_splits(int tiles, int kblocks, int max_blocks) {
-    int first = -1, last_full = -1;
+// Splits of the K/V GEMM: S divides the number of 128-wide k-blocks, keeps at
+// least 8 k-blocks (one per wave) per split when it can, stays within
+// kMaxSplitK (and, at <= 16 rows, within the LDS stage of g), and is the
+// smallest count giving kTargetItems workgroups.
+int choose_kv_splits(int tiles, int kblocks, int64_t M) {
+    int best = -1;
     for (int S = 1; S <= kblocks; ++S) {
-        if (kblocks % S || kblocks / S > max_blocks) continue;
-        if (kblocks / S >= 4) last_full = S;
-        if ((int64_t)tiles * S >= kTargetItems) {
-            first = S;
-            break;
-        }
+        if (kblocks % S) continue;
+        const int nbs = kblocks / S;
+        if (nbs * 128 > kMaxSplitK || (M <= 16 && !stage_fits(M, nbs))) continue;
+        if (best > 0 && nbs < 8) break;
+        best = S;
+        if ((int64_t)tiles * S >= kTargetItems) break;
     }
-    if (first < 0) return last_full > 0 ? last_full : kblocks;
-    if (kblocks / first < 4 && last_full > 0) return last_full;
-    return first;
-}
-
-int max_blocks_for(int64_t M) {
-    const int ng = (int)((M + 15) / 16);
-    return ng <= 1 ? 8 : (ng == 2 ? 4 : 2);
+    return best > 0 ? best : kblocks;
 }
 
 struct Plan {
     int64_t M;
     bool skinny;
-    int S_fc, S_kv;
-    size_t off_part, off_f, off_g, off_ss, off_tfc, off_tkv, off_tg, total;
+    int S_kv;
+    // f [M][H]; small batch: ss [H/16][M] and K/V partials [S][M][O]; large batch: g [M][H]
+    size_t off_f, off_g, off_ss, off_part, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -99,31 +91,21 @@ dfkv_status make_plan(const dfkv_geom *g, int32_t n_reqs, Plan *pl) {
     if (n_reqs < 0) return DFKV_ERR_SHAPE;
     const int64_t M = (int64_t)n_reqs * g->width;
     if (M > (1 << 22)) return DFKV_ERR_SHAPE;
-    const int64_t H = g->hidden, O = out_dim(g), K = k_in(g);
+    const int64_t H = g->hidden, O = out_dim(g);
     Plan p{};
     p.M = M;
     p.skinny = M <= kSkinnyMaxRows;
-    // Tickets first, at offsets that depend only on the geometry: a workspace
-    // shared by calls of different batch sizes always finds them (zeroed) in the
-    // same place.  The data regions after them need no initialisation.
+    const size_t Mp = M > 0 ? (size_t)M : 1;
     size_t off = 0;
-    p.off_tfc = off; off = up256(off + (size_t)(H / 64) * 4);
-    p.off_tkv = off; off = up256(off + (size_t)(O / 64) * 4);
-    p.off_tg = off;  off = up256(off + (size_t)n_groups(g) * 4);
+    p.off_f = off; off = up256(off + Mp * H * 2);
+    p.off_g = off; off = up256(off + Mp * H * 2);
     if (p.skinny) {
-        const int Mp = M > 0 ? (int)M : 1;
-        p.S_fc = choose_splits((int)(H / 64), (int)(K / 128), max_blocks_for(M));
-        p.S_kv = choose_splits((int)(O / 64), (int)(H / 128), max_blocks_for(M));
-        const size_t part_elems = (size_t)(p.S_fc * H > p.S_kv * O ? p.S_fc * H : p.S_kv * O) * Mp;
-        p.off_part = off; off = up256(off + part_elems * 4);
-        p.off_f = off;    off = up256(off + (size_t)Mp * H * 2);
-        p.off_ss = off;   off = up256(off + (size_t)(H / 64) * Mp * 4);
-        p.off_g = 0;
+        p.S_kv = choose_kv_splits((int)(O / 16), (int)(H / 128), M);
+        p.off_ss = off;   off = up256(off + (size_t)(H / 16) * Mp * 4);
+        p.off_part = off; off = up256(off + (size_t)p.S_kv * Mp * O * 4);
     } else {
-        p.S_fc = p.S_kv = 1;
-        p.off_f = off;    off = up256(off + (size_t)M * H * 2);
-        p.off_g = off;    off = up256(off + (size_t)M * H * 2);
-        p.off_part = p.off_ss = 0;
+        p.S_kv = 1;
+        p.off_ss = p.off_part = 0;
     }
     p.total = off;
     *pl = p;
@@ -286,13 +268,13 @@ dfkv_status check_adv_outputs(const dfkv_geom *g, const dfkv_requests *r, const 
     return DFKV_OK;
 }
 
-StoreParams store_params(const dfkv_geom *g, const void *kv, const dfkv_requests *r, const dfkv_pool *pool,
-                         int64_t *slot, uint8_t *wmask, const dfkv_outputs *o) {
-    StoreParams p;
+FinalizeParams fin_params(const dfkv_geom *g, const dfkv_requests *r, const dfkv_pool *pool, const dfkv_outputs *o,
+                          int32_t n_reqs) {
+    FinalizeParams p;
     memset(&p, 0, sizeof p);
-    p.kv = (const uint16_t *)kv;
-    p.kv_ld = out_dim(g);
-    p.B = r->n_reqs;
+    p.O = (int32_t)out_dim(g);
+    p.B = r ? r->n_reqs : n_reqs;
+    p.M = p.B * g->width;
     p.W = g->width;
     p.bs_blk = g->block_size;
     p.pg = g->page_size;
@@ -301,18 +283,20 @@ StoreParams store_params(const dfkv_geom *g, const void *kv, const dfkv_requests
     p.nkv = g->n_kv_heads;
     p.hd = g->head_dim;
     p.per_layer = per_layer(g);
-    p.ctx_len = r->ctx_len_in;
-    p.n_acc = r->n_acc;
-    p.limit = r->alloc_limit;
-    p.dummy = r->is_dummy;
-    p.row_valid = r->row_valid;
-    p.bt = r->block_table;
-    p.bt_stride = r->bt_row_stride;
-    p.bt_cols = r->bt_cols;
-    p.acc = r->accepted_tokens;
-    p.acc_sr = r->acc_stride_req;
-    p.acc_st = r->acc_stride_tok;
-    p.mask_id = r->mask_token_id;
+    if (r) {
+        p.ctx_len = r->ctx_len_in;
+        p.n_acc = r->n_acc;
+        p.limit = r->alloc_limit;
+        p.dummy = r->is_dummy;
+        p.row_valid = r->row_valid;
+        p.bt = r->block_table;
+        p.bt_stride = r->bt_row_stride;
+        p.bt_cols = r->bt_cols;
+        p.acc = r->accepted_tokens;
+        p.acc_sr = r->acc_stride_req;
+        p.acc_st = r->acc_stride_tok;
+        p.mask_id = r->mask_token_id;
+    }
     if (pool) {
         p.num_pages = pool->num_pages;
         for (int l = 0; l < g->n_layers; ++l) {
@@ -323,9 +307,9 @@ StoreParams store_params(const dfkv_geom *g, const void *kv, const dfkv_requests
         p.ss = pool->stride_slot;
         p.sh = pool->stride_head;
     }
-    p.slot = slot;
-    p.wmask = wmask;
     if (o) {
+        p.slot = o->slot;
+        p.wmask = o->write_mask;
         p.c_pos = o->c_pos;
         p.bonus = o->bonus;
         p.emb = o->emb_ids;
@@ -338,59 +322,101 @@ StoreParams store_params(const dfkv_geom *g, const void *kv, const dfkv_requests
 
 // ----- launches ---------------------------------------------------------------
 
-dfkv_status run_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t ld, int32_t n_reqs,
-                        const int32_t *ctx, const float *cs, int32_t cache_len, void *kv_out, uint32_t flags,
-                        void *ws, const Plan &pl, hipStream_t s) {
+// The projection, in two stages.
+//  fc stage  -- f = bf16(hidden . w_fc^T) into ws.  Small batch: streaming GEMM
+//               whose epilogue also writes f's per-16-column sums of squares;
+//               above 16 rows (no LDS stage) or 64 rows (tiled GEMM) also
+//               g = hidden_norm(f) by its own kernel.
+//  K/V stage -- small batch: streaming GEMM (staging g in LDS at <= 16 rows)
+//               into fp32 split partials, then the finalize kernel; large batch:
+//               tiled GEMM over g into kv_out, then the finalize kernel in place.
+// The finalize kernel does k_norm/RoPE (or plain rounding) and, when `fin`
+// asks for it, the paged store and the advance.
+bool stages_g(const Plan &pl) { return pl.skinny && pl.M <= 16; }
+
+dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int64_t ld, const void *w_hnorm,
+                   void *ws, const Plan &pl, hipStream_t s) {
     if (pl.M == 0) return DFKV_OK;
-    const bool fuse = (flags & DFKV_FUSE_NORM_ROPE) != 0;
     char *wsb = (char *)ws;
-    const int64_t K = k_in(g), H = g->hidden, O = out_dim(g);
-    const NormRopeGeom nr = nr_geom(g, w->w_knorm, ctx, cs, cache_len);
+    const int64_t K = k_in(g), H = g->hidden;
+    uint16_t *f = (uint16_t *)(wsb + pl.off_f);
     hipError_t e;
     if (pl.skinny) {
-        SkinnyParams p;
+        StreamParams p;
         memset(&p, 0, sizeof p);
-        p.M = (int32_t)pl.M;
-        p.part = (float *)(wsb + pl.off_part);
-        p.nr = nr;
-        // fc: f = bf16(hidden . w_fc^T), plus per-tile sums of squares
-        p.w = (const uint16_t *)w->w_fc;
+        p.w = (const uint16_t *)w_fc;
         p.x = (const uint16_t *)hidden;
         p.ldx = ld;
+        p.M = (int32_t)pl.M;
         p.K = (int32_t)K;
         p.O = (int32_t)H;
-        p.S = pl.S_fc;
-        p.nb_split = (int32_t)(K / 128 / pl.S_fc);
-        p.ticket = (int32_t *)(wsb + pl.off_tfc);
-        p.f_out = (uint16_t *)(wsb + pl.off_f);
+        p.S = 1;
+        p.nbs = (int32_t)(K / 128);
+        p.out = f;
         p.ss_out = (float *)(wsb + pl.off_ss);
-        if ((e = launch_skinny(p, SK_FC, s)) != hipSuccess) return hip_status(e);
-        // stacked K/V GEMM with hidden_norm applied on load, optional k_norm + RoPE epilogue
+        e = launch_stream(p, s);
+    } else {
+        TiledParams t{(const uint16_t *)hidden, ld, (const uint16_t *)w_fc, f, H, (int32_t)pl.M, (int32_t)K,
+                      (int32_t)H};
+        e = launch_tiled(t, s);
+    }
+    if (e != hipSuccess) return hip_status(e);
+    if (stages_g(pl)) return DFKV_OK;
+    uint16_t *gb = (uint16_t *)(wsb + pl.off_g);
+    return hip_status(launch_hidden_norm(f, (const uint16_t *)w_hnorm, gb, (int)pl.M, (int)H, g->eps, s));
+}
+
+dfkv_status run_kv(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx, const float *cs, int32_t cache_len,
+                   void *kv_out, bool fuse, void *ws, const Plan &pl, FinalizeParams fin, bool need_finalize,
+                   hipStream_t s) {
+    if (pl.M == 0) return DFKV_OK;
+    char *wsb = (char *)ws;
+    const int64_t H = g->hidden, O = out_dim(g);
+    hipError_t e;
+    fin.nr = nr_geom(g, w->w_knorm, ctx, cs, cache_len);
+    fin.norm = fuse ? 1 : 0;
+    fin.kv_out = (uint16_t *)kv_out;
+    if (pl.skinny) {
+        StreamParams p;
+        memset(&p, 0, sizeof p);
         p.w = (const uint16_t *)w->w_kv;
-        p.x = (const uint16_t *)(wsb + pl.off_f);
         p.ldx = H;
+        p.M = (int32_t)pl.M;
         p.K = (int32_t)H;
         p.O = (int32_t)O;
         p.S = pl.S_kv;
-        p.nb_split = (int32_t)(H / 128 / pl.S_kv);
-        p.ticket = (int32_t *)(wsb + pl.off_tkv);
-        p.w_hn = (const uint16_t *)w->w_hnorm;
-        p.ss_in = (const float *)(wsb + pl.off_ss);
-        p.kv_out = (uint16_t *)kv_out;
-        p.gticket = (int32_t *)(wsb + pl.off_tg);
-        p.fuse = fuse ? 1 : 0;
-        if ((e = launch_skinny(p, SK_KV, s)) != hipSuccess) return hip_status(e);
-        return DFKV_OK;
+        p.nbs = (int32_t)(H / 128 / pl.S_kv);
+        p.part = (float *)(wsb + pl.off_part);
+        if (stages_g(pl)) {
+            p.x = (const uint16_t *)(wsb + pl.off_f);
+            p.w_hn = (const uint16_t *)w->w_hnorm;
+            p.ss_in = (const float *)(wsb + pl.off_ss);
+            p.T_in = (int32_t)(H / 16);
+            p.eps = g->eps;
+        } else {
+            p.x = (const uint16_t *)(wsb + pl.off_g);
+        }
+        if ((e = launch_stream(p, s)) != hipSuccess) return hip_status(e);
+        fin.part = p.part;
+        fin.S = pl.S_kv;
+        fin.src = nullptr;
+        return hip_status(launch_finalize(fin, s));
     }
-    uint16_t *f = (uint16_t *)(wsb + pl.off_f), *gb = (uint16_t *)(wsb + pl.off_g);
-    TiledParams t{(const uint16_t *)hidden, ld, (const uint16_t *)w->w_fc, f, H, (int32_t)pl.M, (int32_t)K, (int32_t)H};
-    if ((e = launch_tiled(t, s)) != hipSuccess) return hip_status(e);
-    if ((e = launch_hidden_norm(f, (const uint16_t *)w->w_hnorm, gb, (int)pl.M, (int)H, g->eps, s)) != hipSuccess)
-        return hip_status(e);
+    const uint16_t *gb = (const uint16_t *)(wsb + pl.off_g);
     TiledParams t2{gb, H, (const uint16_t *)w->w_kv, (uint16_t *)kv_out, O, (int32_t)pl.M, (int32_t)H, (int32_t)O};
     if ((e = launch_tiled(t2, s)) != hipSuccess) return hip_status(e);
-    if (fuse && (e = launch_norm_rope(nr, (uint16_t *)kv_out, (int)pl.M, s)) != hipSuccess) return hip_status(e);
-    return DFKV_OK;
+    if (!fuse && !need_finalize) return DFKV_OK;
+    fin.part = nullptr;
+    fin.src = (const uint16_t *)kv_out;  // in place: each element is read and written by one thread
+    return hip_status(launch_finalize(fin, s));
+}
+
+dfkv_status run_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t ld, const int32_t *ctx,
+                        const float *cs, int32_t cache_len, void *kv_out, bool fuse, void *ws, const Plan &pl,
+                        const FinalizeParams &fin, bool need_finalize, hipStream_t s) {
+    dfkv_status st = run_fc(g, w->w_fc, hidden, ld, w->w_hnorm, ws, pl, s);
+    if (st != DFKV_OK) return st;
+    return run_kv(g, w, ctx, cs, cache_len, kv_out, fuse, ws, pl, fin, need_finalize, s);
 }
 
 }  // namespace
@@ -447,8 +473,60 @@ dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *
     dfkv_status st = check_project(g, w, hidden, hidden_row_stride, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out,
                                    flags, ws, ws_bytes, &pl);
     if (st != DFKV_OK) return st;
-    return run_project(g, w, hidden, hidden_row_stride, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out, flags, ws, pl,
-                       (hipStream_t)stream);
+    const FinalizeParams fin = fin_params(g, nullptr, nullptr, nullptr, n_reqs);
+    return run_project(g, w, hidden, hidden_row_stride, ctx_len_in, cos_sin, cache_len, kv_out,
+                       (flags & DFKV_FUSE_NORM_ROPE) != 0, ws, pl, fin, false, (hipStream_t)stream);
+}
+
+dfkv_status dfkv_project_fc(const dfkv_geom *g, const void *w_fc, const void *w_hnorm, const void *hidden,
+                            int64_t hidden_row_stride, int32_t n_reqs, void *ws, size_t ws_bytes,
+                            dfkv_stream_t stream) {
+    if (!g) return DFKV_ERR_NULL;
+    Plan pl;
+    dfkv_status st = make_plan(g, n_reqs, &pl);
+    if (st != DFKV_OK) return st;
+    if (pl.M == 0) return DFKV_OK;
+    if (!w_fc || !hidden || !ws || !w_hnorm) return DFKV_ERR_NULL;
+    const int64_t K = k_in(g), H = g->hidden, M = pl.M;
+    if (hidden_row_stride < K || (hidden_row_stride * 2) % 16 != 0) return DFKV_ERR_LAYOUT;
+    if (!al16(hidden) || !al16(w_fc) || !al16(ws) || !al16(w_hnorm)) return DFKV_ERR_LAYOUT;
+    if (ws_bytes < pl.total) return DFKV_ERR_WORKSPACE;
+    const size_t hid_bytes = (size_t)((M - 1) * hidden_row_stride + K) * 2;
+    if (overlap(ws, ws_bytes, hidden, hid_bytes) || overlap(ws, ws_bytes, w_fc, (size_t)H * K * 2) ||
+        overlap(ws, ws_bytes, w_hnorm, (size_t)H * 2))
+        return DFKV_ERR_ALIAS;
+    return run_fc(g, w_fc, hidden, hidden_row_stride, w_hnorm, ws, pl, (hipStream_t)stream);
+}
+
+dfkv_status dfkv_project_kv(const dfkv_geom *g, const dfkv_weights *w, int32_t n_reqs, const int32_t *ctx_len_in,
+                            const float *cos_sin, int32_t cache_len, void *kv_out, uint32_t flags, void *ws,
+                            size_t ws_bytes, dfkv_stream_t stream) {
+    if (!g || !w) return DFKV_ERR_NULL;
+    Plan pl;
+    dfkv_status st = make_plan(g, n_reqs, &pl);
+    if (st != DFKV_OK) return st;
+    if ((flags & ~(uint32_t)DFKV_FUSE_NORM_ROPE) != 0) return DFKV_ERR_SHAPE;
+    if (pl.M == 0) return DFKV_OK;
+    const bool fuse = (flags & DFKV_FUSE_NORM_ROPE) != 0;
+    if (!kv_out || !w->w_hnorm || !w->w_kv || !ws) return DFKV_ERR_NULL;
+    if (fuse && (!w->w_knorm || !ctx_len_in || !cos_sin)) return DFKV_ERR_NULL;
+    if (fuse && cache_len <= 0) return DFKV_ERR_SHAPE;
+    const int64_t H = g->hidden, O = out_dim(g), M = pl.M;
+    if (!al16(kv_out) || !al16(w->w_hnorm) || !al16(w->w_kv) || !al16(ws)) return DFKV_ERR_LAYOUT;
+    if (fuse && (!al4(cos_sin) || ((uintptr_t)w->w_knorm & 1u))) return DFKV_ERR_LAYOUT;
+    if (ws_bytes < pl.total) return DFKV_ERR_WORKSPACE;
+    const size_t kv_bytes = (size_t)M * O * 2;
+    if (overlap(kv_out, kv_bytes, ws, ws_bytes) || overlap(kv_out, kv_bytes, w->w_kv, (size_t)O * H * 2) ||
+        overlap(kv_out, kv_bytes, w->w_hnorm, (size_t)H * 2))
+        return DFKV_ERR_ALIAS;
+    if (fuse) {
+        const size_t kn = (size_t)g->n_layers * (g->kind == DFKV_GQA ? g->head_dim : g->latent_dim) * 2;
+        if (overlap(kv_out, kv_bytes, cos_sin, (size_t)cache_len * g->rope_dim * 4) ||
+            overlap(kv_out, kv_bytes, w->w_knorm, kn) || overlap(kv_out, kv_bytes, ctx_len_in, (size_t)n_reqs * 4))
+            return DFKV_ERR_ALIAS;
+    }
+    const FinalizeParams fin = fin_params(g, nullptr, nullptr, nullptr, n_reqs);
+    return run_kv(g, w, ctx_len_in, cos_sin, cache_len, kv_out, fuse, ws, pl, fin, false, (hipStream_t)stream);
 }
 
 dfkv_status dfkv_norm_rope(const dfkv_geom *g, const void *w_knorm, int32_t n_reqs, const int32_t *ctx_len_in,
@@ -465,8 +543,12 @@ dfkv_status dfkv_norm_rope(const dfkv_geom *g, const void *w_knorm, int32_t n_re
     if (overlap(kv, kvb, cos_sin, (size_t)cache_len * g->rope_dim * 4) || overlap(kv, kvb, w_knorm, kn) ||
         overlap(kv, kvb, ctx_len_in, (size_t)n_reqs * 4))
         return DFKV_ERR_ALIAS;
-    const NormRopeGeom nr = nr_geom(g, w_knorm, ctx_len_in, cos_sin, cache_len);
-    return hip_status(launch_norm_rope(nr, (uint16_t *)kv, (int)N, (hipStream_t)stream));
+    FinalizeParams fin = fin_params(g, nullptr, nullptr, nullptr, n_reqs);
+    fin.nr = nr_geom(g, w_knorm, ctx_len_in, cos_sin, cache_len);
+    fin.norm = 1;
+    fin.src = (const uint16_t *)kv;
+    fin.kv_out = (uint16_t *)kv;  // in place: each element is read and written by one thread
+    return hip_status(launch_finalize(fin, (hipStream_t)stream));
 }
 
 dfkv_status dfkv_paged_store(const dfkv_geom *g, const void *kv, const dfkv_requests *req, const dfkv_pool *pool,
@@ -477,8 +559,12 @@ dfkv_status dfkv_paged_store(const dfkv_geom *g, const void *kv, const dfkv_requ
     if (req->n_reqs == 0) return DFKV_OK;
     if ((st = check_pool(g, pool)) != DFKV_OK) return st;
     if ((st = check_store_outputs(g, req, pool, kv, slot_out, write_mask_out)) != DFKV_OK) return st;
-    const StoreParams p = store_params(g, kv, req, pool, slot_out, write_mask_out, nullptr);
-    return hip_status(launch_store_advance(p, true, false, (hipStream_t)stream));
+    FinalizeParams p = fin_params(g, req, pool, nullptr, 0);
+    p.slot = slot_out;
+    p.wmask = write_mask_out;
+    p.src = (const uint16_t *)kv;
+    p.store = 1;
+    return hip_status(launch_finalize(p, (hipStream_t)stream));
 }
 
 dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfkv_outputs *out, dfkv_stream_t stream) {
@@ -487,8 +573,8 @@ dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfk
     if ((st = check_requests(g, req, false, true)) != DFKV_OK) return st;
     if (req->n_reqs == 0) return DFKV_OK;
     if ((st = check_adv_outputs(g, req, out)) != DFKV_OK) return st;
-    const StoreParams p = store_params(g, nullptr, req, nullptr, nullptr, nullptr, out);
-    return hip_status(launch_store_advance(p, false, true, (hipStream_t)stream));
+    const FinalizeParams p = fin_params(g, req, nullptr, out, 0);
+    return hip_status(launch_advance(p, (hipStream_t)stream));
 }
 
 static dfkv_status check_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
@@ -523,8 +609,11 @@ dfkv_status dfkv_store_advance(const dfkv_geom *g, const void *kv, const dfkv_re
     dfkv_status st = check_store_advance(g, kv, req, pool, out);
     if (st != DFKV_OK) return st;
     if (req->n_reqs == 0) return DFKV_OK;
-    const StoreParams p = store_params(g, kv, req, pool, out->slot, out->write_mask, out);
-    return hip_status(launch_store_advance(p, true, true, (hipStream_t)stream));
+    FinalizeParams p = fin_params(g, req, pool, out, 0);
+    p.src = (const uint16_t *)kv;
+    p.store = 1;
+    p.advance = 1;
+    return hip_status(launch_finalize(p, (hipStream_t)stream));
 }
 
 dfkv_status dfkv_step(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t hidden_row_stride,
@@ -549,11 +638,12 @@ dfkv_status dfkv_step(const dfkv_geom *g, const dfkv_weights *w, const void *hid
         if (overlap(outs[i], ob[i], ws, ws_bytes) || overlap(outs[i], ob[i], hidden, hid_bytes) ||
             overlap(outs[i], ob[i], cos_sin, (size_t)cache_len * g->rope_dim * 4))
             return DFKV_ERR_ALIAS;
-    st = run_project(g, w, hidden, hidden_row_stride, req->n_reqs, req->ctx_len_in, cos_sin, cache_len, kv_out,
-                     DFKV_FUSE_NORM_ROPE, ws, pl, (hipStream_t)stream);
-    if (st != DFKV_OK) return st;
-    const StoreParams p = store_params(g, kv_out, req, pool, out->slot, out->write_mask, out);
-    return hip_status(launch_store_advance(p, true, true, (hipStream_t)stream));
+    // projection with the finalize kernel doing k_norm/RoPE, the store and the advance
+    FinalizeParams fin = fin_params(g, req, pool, out, 0);
+    fin.store = 1;
+    fin.advance = 1;
+    return run_project(g, w, hidden, hidden_row_stride, req->ctx_len_in, cos_sin, cache_len, kv_out, true, ws, pl,
+                       fin, true, (hipStream_t)stream);
 }
 
 }  // extern "C"

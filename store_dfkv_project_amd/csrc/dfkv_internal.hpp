@@ -39,8 +39,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
-// Projection epilogue helpers shared by the standalone norm/RoPE kernel and
-// the GEMM epilogues.  One wave handles one (row, head) or one (row, layer).
+// Geometry of the k_norm / RoPE epilogue.
 // ---------------------------------------------------------------------------
 
 struct NormRopeGeom {
@@ -52,77 +51,12 @@ struct NormRopeGeom {
     const float *cos_sin;
 };
 
+// cos/sin cache row of token row `row`: position ctx_len_in[r] + i, clamped to the cache.
 __device__ __forceinline__ const float *rope_row(const NormRopeGeom &g, int row) {
-    int r = row / g.width, i = row - r * g.width;
-    int64_t pos = (int64_t)g.ctx_len_in[r] + i;
-    int64_t p = pos < 0 ? 0 : (pos > g.cache_len - 1 ? g.cache_len - 1 : pos);
+    const int r = row / g.width, i = row - r * g.width;
+    const int64_t pos = (int64_t)g.ctx_len_in[r] + i;
+    const int64_t p = pos < 0 ? 0 : (pos > g.cache_len - 1 ? g.cache_len - 1 : pos);
     return g.cos_sin + p * g.rope_dim;
-}
-
-// GQA K head of hd (<= 256) elements at `x` (bf16, in place), layer l.
-// Lane handles the NeoX pairs (j, j + hd/2) for j = lane, lane + 64.
-__device__ __forceinline__ void norm_rope_gqa_head(const NormRopeGeom &g, uint16_t *x, int l, int row, int lane) {
-    const int half = g.hd >> 1;
-    float a[2], b[2];
-    float ss = 0.f;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        int j = lane + q * kWave;
-        a[q] = b[q] = 0.f;
-        if (j < half) {
-            a[q] = bf2f(x[j]);
-            b[q] = bf2f(x[j + half]);
-            ss += a[q] * a[q] + b[q] * b[q];
-        }
-    }
-    ss = wave_sum(ss);
-    const float rinv = 1.0f / sqrtf(ss / (float)g.hd + g.eps);
-    const float *cs = rope_row(g, row);
-    const uint16_t *wk = g.w_knorm + (int64_t)l * g.hd;
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        int j = lane + q * kWave;
-        if (j < half) {
-            float ua = bf2f(f2bf(bf2f(wk[j]) * (a[q] * rinv)));
-            float ub = bf2f(f2bf(bf2f(wk[j + half]) * (b[q] * rinv)));
-            float c = cs[j], s = cs[half + j];
-            x[j] = f2bf(ua * c - ub * s);
-            x[j + half] = f2bf(ub * c + ua * s);
-        }
-    }
-}
-
-// MLA layer slice at `x`: latent (RMSNorm with w_knorm[l]) then rope part (rotation only).
-__device__ __forceinline__ void norm_rope_mla_layer(const NormRopeGeom &g, uint16_t *x, int l, int row, int lane) {
-    const int R = g.latent;
-    float v[16];  // R <= 1024
-    float ss = 0.f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        int e = lane + q * kWave;
-        v[q] = 0.f;
-        if (e < R) {
-            v[q] = bf2f(x[e]);
-            ss += v[q] * v[q];
-        }
-    }
-    ss = wave_sum(ss);
-    const float rinv = 1.0f / sqrtf(ss / (float)R + g.eps);
-    const uint16_t *wk = g.w_knorm + (int64_t)l * R;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-        int e = lane + q * kWave;
-        if (e < R) x[e] = f2bf(bf2f(wk[e]) * (v[q] * rinv));
-    }
-    const int half = g.rope_dim >> 1;  // <= 64
-    if (lane < half) {
-        const float *cs = rope_row(g, row);
-        uint16_t *rp = x + R;
-        float a = bf2f(rp[lane]), b = bf2f(rp[lane + half]);
-        float c = cs[lane], s = cs[half + lane];
-        rp[lane] = f2bf(a * c - b * s);
-        rp[lane + half] = f2bf(b * c + a * s);
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -133,18 +67,25 @@ __device__ __forceinline__ void norm_rope_mla_layer(const NormRopeGeom &g, uint1
 // status of this launch alone (hipLaunchKernel; the process-wide "last error" that
 // other code may have left behind is neither read nor cleared).
 template <typename P>
-inline hipError_t launch1(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s, const P &p) {
+inline hipError_t launch1(void (*kernel)(P), dim3 grid, dim3 block, hipStream_t s, const P &p, size_t shmem = 0) {
     P copy = p;
     void *args[] = {(void *)&copy};
-    return hipLaunchKernel((const void *)kernel, grid, block, args, 0, s);
+    return hipLaunchKernel((const void *)kernel, grid, block, args, shmem, s);
 }
 
 // Record a failed HIP call for dfkv_hip_error_string (per host thread).
 void note_hip_error(hipError_t e);
 
-struct StoreParams {
-    const uint16_t *kv;
-    int64_t kv_ld;
+// Finalize: k_norm/RoPE + paged store + advance (one workgroup per row x layer).
+struct FinalizeParams {
+    // source rows of the stacked projection: fp32 split-K partials [S][M][O], or bf16 rows [N][O]
+    const float *part;
+    int32_t S, M, O;
+    const uint16_t *src;
+    uint16_t *kv_out;  // final bf16 rows [N][O], or NULL
+    int32_t norm, store, advance;
+    NormRopeGeom nr;
+    // request state
     int32_t B, W, bs_blk, pg, L, kind, nkv, hd, per_layer;
     const int32_t *ctx_len, *n_acc, *limit;
     const uint8_t *dummy, *row_valid;
@@ -154,42 +95,42 @@ struct StoreParams {
     const int32_t *acc;
     int64_t acc_sr, acc_st;
     int32_t mask_id;
+    // pools
     uint16_t *pk[DFKV_MAX_LAYERS];
     uint16_t *pv[DFKV_MAX_LAYERS];
     int64_t sp, ss, sh;
+    // outputs
     int64_t *slot;
     uint8_t *wmask;
     int32_t *c_pos, *bonus, *emb, *q_pos, *ctx_out, *seq_len;
 };
-hipError_t launch_store_advance(const StoreParams &p, bool store, bool advance, hipStream_t s);
+hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s);
+hipError_t launch_advance(const FinalizeParams &p, hipStream_t s);
 
-hipError_t launch_norm_rope(const NormRopeGeom &g, uint16_t *kv, int n_rows, hipStream_t s);
 hipError_t launch_hidden_norm(const uint16_t *f, const uint16_t *w, uint16_t *g, int n_rows, int H, float eps,
                               hipStream_t s);
 hipError_t launch_rope_cache(const dfkv_rope &r, float *cs, int cache_len, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
-// Skinny split-K projection GEMM (M <= 64 token rows).
-enum { SK_FC = 0, SK_KV = 1 };
-struct SkinnyParams {
-    const uint16_t *w;   // [O][K]
-    const uint16_t *x;   // FC: hidden rows (ldx); KV: f rows [M][K]
+// Weight-streaming projection GEMM (M <= 64 token rows).
+constexpr int kMaxSplitK = 8192;    // largest k extent of one K/V split
+constexpr int kStageChunks = 4;     // 16-byte chunks of f each of 512 threads stages
+// Whether a K/V split of nbs k-blocks over M rows stages g = hidden_norm(f) in LDS (<= 32 KB).
+inline bool stage_fits(int64_t M, int nbs) { return M <= 16 && M * nbs * 16 <= 512 * kStageChunks; }
+struct StreamParams {
+    const uint16_t *w;  // [O][K] weights
+    const uint16_t *x;  // activation rows (row stride ldx): hidden for fc; f (staged) or g for the K/V GEMM
     int64_t ldx;
-    int32_t M, K, O, S, nb_split;  // k-blocks of 128 per split
-    float *part;                   // [S][O][M]
-    int32_t *ticket;               // [O/64]
-    // FC epilogue
-    uint16_t *f_out;   // [M][O]
-    float *ss_out;     // [O/64][M]
-    // KV prologue (hidden_norm) and epilogue
-    const uint16_t *w_hn;
-    const float *ss_in;  // [K/64][M]
-    uint16_t *kv_out;    // [M][O]
-    int32_t *gticket;    // norm-group tickets
-    int32_t fuse;
-    NormRopeGeom nr;
+    int32_t M, K, O, S, nbs;  // nbs: 128-wide k-blocks per split
+    uint16_t *out;            // fc: f [M][O] (S == 1), or NULL
+    float *ss_out;            // fc: per 16-column tile sums of squares of f [O/16][M]
+    const uint16_t *w_hn;     // K/V staging: hidden_norm weight [K]
+    const float *ss_in;       // K/V staging: [T_in][M] sums of squares of f
+    int32_t T_in;
+    float eps;
+    float *part;              // K/V: fp32 [S][M][O] partial sums (out == NULL)
 };
-hipError_t launch_skinny(const SkinnyParams &p, int mode, hipStream_t s);
+hipError_t launch_stream(const StreamParams &p, hipStream_t s);
 
 // Tiled MFMA GEMM for larger M: out[n][o] = bf16(sum_k x[n][k] w[o][k]).
 struct TiledParams {

@@ -1,0 +1,293 @@
+// k_finalize.hip -- the last kernel of a step: k_norm + RoPE, the paged store of
+// the gen tokens' context K/V into every layer's pool, and the per-request
+// advance, in one launch.
+//
+// Sources (page titles and sections):
+//  * TensorRT-LLM PR #20550 "fuse the decode-step drafter bookkeeping into
+//    Triton kernels", section TLLM_DFLASH_FUSED_PROLOGUE: rejected-row mask,
+//    clamp to the request's allocation, page lookup, write to every layer; the
+//    ctx_len advance with the clamp, the dummy-slot reset and the advertised
+//    context length; bonus token, query/context positions, embedding ids.  The
+//    downstream commit quoted on that page adds seq_lens and requires pool
+//    entries outside the step's destinations to stay unchanged.
+//  * TensorRT-LLM PR #13995 "DFlash performance optimizations": commit "fuse
+//    cross-layer k_norm" (one RMSNorm over every K head times stacked per-layer
+//    weights, one eps) and commit "match RoPE between context and query for
+//    YaRN" (context K rotated from the one cos/sin cache).
+//
+// One workgroup per (token row, drafter layer).  The row's stacked projection
+// for that layer is read either as fp32 split-K partial sums (summed in split
+// order, then rounded to bf16 -- the K/V GEMM output) or as bf16 rows.  With
+// `norm`, each K head (GQA) or the latent (MLA) is RMS-normalised by one wave
+// (wave-level reduction) and rotated (NeoX pairs held by one lane), the rope
+// part of MLA rotated only; V passes through.  The result goes to kv_out
+// and, when the row's write predicate holds, to the layer's pool.  Rows whose
+// predicate fails never touch the pools.
+#include "dfkv_internal.hpp"
+
+namespace dfkv {
+
+// Write predicate and slot of token i of request r (row = r*W + i).  The request's
+// fields are loaded together; only the block-table entry depends on them.
+__device__ __forceinline__ bool row_destination(const FinalizeParams &p, int r, int i, int row, int64_t &slot) {
+    const uint8_t d = p.dummy[r];
+    const int32_t n = p.n_acc[r];
+    const int32_t c = p.ctx_len[r];
+    const int32_t lim = p.limit[r];
+    const uint8_t rv = p.row_valid ? p.row_valid[row] : (uint8_t)1;
+    slot = -1;
+    const int64_t pos = (int64_t)c + i;
+    if (d || !(i < n) || !rv || pos < 0 || pos >= (int64_t)lim) return false;
+    const int64_t pidx = pos / p.pg;
+    if (pidx >= p.bt_cols) return false;
+    const int32_t page = p.bt[(int64_t)r * p.bt_stride + pidx];
+    if (page < 0 || page >= p.num_pages) return false;
+    slot = (int64_t)page * p.pg + (pos - pidx * p.pg);
+    return true;
+}
+
+__device__ __forceinline__ void request_advance(const FinalizeParams &p, int r) {
+    const int32_t c = p.ctx_len[r], n = p.n_acc[r], lim = p.limit[r];
+    const bool d = p.dummy[r] != 0;
+    const int64_t adv = (int64_t)c + n;
+    const int32_t ctx_new = d ? 0 : (int32_t)(adv < (int64_t)lim ? adv : (int64_t)lim);
+    const int nb = n < 1 ? 1 : (n > p.W ? p.W : n);
+    const int32_t bonus = p.acc[(int64_t)r * p.acc_sr + (int64_t)(nb - 1) * p.acc_st];
+    for (int j = threadIdx.x; j < p.bs_blk; j += blockDim.x) {
+        p.emb[(int64_t)r * p.bs_blk + j] = j == 0 ? bonus : p.mask_id;
+        p.q_pos[(int64_t)r * p.bs_blk + j] = ctx_new + j;
+    }
+    for (int j = threadIdx.x; j < p.W; j += blockDim.x) p.c_pos[(int64_t)r * p.W + j] = (int32_t)((int64_t)c + j);
+    if (threadIdx.x == 0) {
+        p.bonus[r] = bonus;
+        p.ctx_out[r] = ctx_new;
+        p.seq_len[r] = ctx_new + p.bs_blk;
+    }
+}
+
+// one element of the row's stacked projection, as fp32 (the bf16-rounded GEMM output)
+__device__ __forceinline__ float load_y(const FinalizeParams &p, int row, int64_t col) {
+    if (p.part) {
+        float y = 0.f;
+        for (int s = 0; s < p.S; ++s) y += p.part[((int64_t)s * p.M + row) * p.O + col];
+        return bf2f(f2bf(y));
+    }
+    return bf2f(p.src[(int64_t)row * p.O + col]);
+}
+
+// 8 consecutive elements (16 B aligned) of the row, as bf16 bits
+__device__ __forceinline__ u32x4 load_y8(const FinalizeParams &p, int row, int64_t col) {
+    if (p.part) {
+        float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < p.S; ++s) {
+            const f32x4 *src = (const f32x4 *)(p.part + ((int64_t)s * p.M + row) * p.O + col);
+            const f32x4 lo = src[0], hi = src[1];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                y[e] += lo[e];
+                y[4 + e] += hi[e];
+            }
+        }
+        return u32x4{pack2(y[0], y[1]), pack2(y[2], y[3]), pack2(y[4], y[5]), pack2(y[6], y[7])};
+    }
+    return *(const u32x4 *)(p.src + (int64_t)row * p.O + col);
+}
+
+constexpr int kFinThreads = 512;  // 8 waves: one K head per wave for up to 8 KV heads
+
+__global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p) {
+    const int L = p.L;
+    const int row = blockIdx.x / L, l = blockIdx.x - (blockIdx.x / L) * L;
+    const int r = row / p.W, i = row - (row / p.W) * p.W;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    constexpr int NW = kFinThreads / 64;
+
+    if (p.advance && i == 0 && l == 0) request_advance(p, r);
+    const int64_t lay = (int64_t)l * p.per_layer;
+    uint16_t *const out = p.kv_out ? p.kv_out + (int64_t)row * p.O + lay : nullptr;
+
+    if (!p.norm) {
+        // final K/V rows in hand (paged store of a finished projection, or plain rounding of the
+        // partial sums): 16-byte chunks straight through, pool writes only for written rows
+        int64_t slot = -1;
+        const bool w = p.store && row_destination(p, r, i, row, slot);
+        if (p.store && l == 0 && tid == 0) {
+            p.slot[row] = slot;
+            p.wmask[row] = w ? 1 : 0;
+        }
+        if (!out && !w) return;
+        int64_t dst0 = 0;
+        if (w) {
+            const int64_t page = slot / p.pg;
+            dst0 = page * p.sp + (slot - page * p.pg) * p.ss;
+        }
+        const int nch = p.per_layer >> 3;
+        for (int c = tid; c < nch; c += kFinThreads) {
+            const int e = c << 3;
+            const u32x4 v = load_y8(p, row, lay + e);
+            if (out) *(u32x4 *)(out + e) = v;
+            if (w) {
+                if (p.kind == DFKV_GQA) {
+                    const int kvh = p.nkv * p.hd;
+                    const bool is_v = e >= kvh;
+                    const int ee = is_v ? e - kvh : e;
+                    const int h = ee / p.hd;
+                    *(u32x4 *)((is_v ? p.pv[l] : p.pk[l]) + dst0 + (int64_t)h * p.sh + (ee - h * p.hd)) = v;
+                } else {
+                    *(u32x4 *)(p.pk[l] + dst0 + e) = v;
+                }
+            }
+        }
+        return;
+    }
+
+    if (p.kind == DFKV_GQA) {
+        const int hd = p.hd, nkv = p.nkv, half = hd >> 1;
+        const int kvh = nkv * hd;
+        // 1. independent loads first: this thread's V chunk and this wave's first K head
+        const int vch = kvh >> 3;
+        u32x4 vv = u32x4{0u, 0u, 0u, 0u};
+        if (tid < vch) vv = load_y8(p, row, lay + kvh + (tid << 3));
+        float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
+        int h = wave;
+        if (h < nkv) {
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int j = lane + q2 * 64;
+                if (j < half) {
+                    a[q2] = load_y(p, row, lay + h * hd + j);
+                    b[q2] = load_y(p, row, lay + h * hd + j + half);
+                }
+            }
+        }
+        // 2. the row's destination
+        int64_t slot = -1;
+        const bool w = p.store && row_destination(p, r, i, row, slot);
+        if (p.store && l == 0 && tid == 0) {
+            p.slot[row] = slot;
+            p.wmask[row] = w ? 1 : 0;
+        }
+        int64_t dst0 = 0;
+        if (w) {
+            const int64_t page = slot / p.pg;
+            dst0 = page * p.sp + (slot - page * p.pg) * p.ss;
+        }
+        // 3. V straight through
+        for (int c = tid; c < vch; c += kFinThreads) {
+            const u32x4 v = c == tid ? vv : load_y8(p, row, lay + kvh + (c << 3));
+            const int hh = c / (hd >> 3), e = (c - hh * (hd >> 3)) << 3;
+            if (out) *(u32x4 *)(out + kvh + (c << 3)) = v;
+            if (w) *(u32x4 *)(p.pv[l] + dst0 + (int64_t)hh * p.sh + e) = v;
+        }
+        // 4. K heads: k_norm then RoPE, one wave per head
+        const float *cs = rope_row(p.nr, row);
+        const uint16_t *wk = p.nr.w_knorm + (int64_t)l * hd;
+        for (; h < nkv; h += NW) {
+            if (h != wave) {
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    const int j = lane + q2 * 64;
+                    a[q2] = b[q2] = 0.f;
+                    if (j < half) {
+                        a[q2] = load_y(p, row, lay + h * hd + j);
+                        b[q2] = load_y(p, row, lay + h * hd + j + half);
+                    }
+                }
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) ss += a[q2] * a[q2] + b[q2] * b[q2];
+            ss = wave_sum(ss);
+            const float rinv = 1.0f / sqrtf(ss / (float)hd + p.nr.eps);
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int j = lane + q2 * 64;
+                if (j < half) {
+                    const float ua = bf2f(f2bf(bf2f(wk[j]) * (a[q2] * rinv)));
+                    const float ub = bf2f(f2bf(bf2f(wk[j + half]) * (b[q2] * rinv)));
+                    const float c = cs[j], sn = cs[half + j];
+                    const uint16_t ka = f2bf(ua * c - ub * sn), kb = f2bf(ub * c + ua * sn);
+                    if (out) {
+                        out[h * hd + j] = ka;
+                        out[h * hd + j + half] = kb;
+                    }
+                    if (w) {
+                        uint16_t *d = p.pk[l] + dst0 + (int64_t)h * p.sh;
+                        d[j] = ka;
+                        d[j + half] = kb;
+                    }
+                }
+            }
+        }
+    } else {
+        // MLA: wave 0 normalises the latent and rotates the rope part
+        if (wave != 0) return;
+        const int R = p.nr.latent, P = p.nr.rope_dim, half = P >> 1;
+        float v[16];
+#pragma unroll
+        for (int q2 = 0; q2 < 16; ++q2) {
+            const int e = lane + q2 * 64;
+            v[q2] = e < R ? load_y(p, row, lay + e) : 0.f;
+        }
+        float ra = 0.f, rb = 0.f;
+        if (lane < half) {
+            ra = load_y(p, row, lay + R + lane);
+            rb = load_y(p, row, lay + R + lane + half);
+        }
+        int64_t slot = -1;
+        const bool w = p.store && row_destination(p, r, i, row, slot);
+        if (p.store && l == 0 && lane == 0) {
+            p.slot[row] = slot;
+            p.wmask[row] = w ? 1 : 0;
+        }
+        uint16_t *d = nullptr;
+        if (w) {
+            const int64_t page = slot / p.pg;
+            d = p.pk[l] + page * p.sp + (slot - page * p.pg) * p.ss;
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int q2 = 0; q2 < 16; ++q2) ss += v[q2] * v[q2];
+        ss = wave_sum(ss);
+        const float rinv = 1.0f / sqrtf(ss / (float)R + p.nr.eps);
+        const uint16_t *wk = p.nr.w_knorm + (int64_t)l * R;
+#pragma unroll
+        for (int q2 = 0; q2 < 16; ++q2) {
+            const int e = lane + q2 * 64;
+            if (e < R) {
+                const uint16_t o = f2bf(bf2f(wk[e]) * (v[q2] * rinv));
+                if (out) out[e] = o;
+                if (d) d[e] = o;
+            }
+        }
+        if (lane < half) {
+            const float *cs = rope_row(p.nr, row);
+            const float c = cs[lane], sn = cs[half + lane];
+            const uint16_t ka = f2bf(ra * c - rb * sn), kb = f2bf(rb * c + ra * sn);
+            if (out) {
+                out[R + lane] = ka;
+                out[R + lane + half] = kb;
+            }
+            if (d) {
+                d[R + lane] = ka;
+                d[R + lane + half] = kb;
+            }
+        }
+    }
+}
+
+// Advance only: one workgroup per request.
+__global__ __launch_bounds__(64) void k_advance(const FinalizeParams p) { request_advance(p, blockIdx.x); }
+
+hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s) {
+    const int64_t N = (int64_t)p.B * p.W;
+    if (N == 0) return hipSuccess;
+    return launch1(k_finalize, dim3((unsigned)(N * p.L)), dim3(kFinThreads), s, p);
+}
+
+hipError_t launch_advance(const FinalizeParams &p, hipStream_t s) {
+    if (p.B == 0) return hipSuccess;
+    return launch1(k_advance, dim3(p.B), dim3(64), s, p);
+}
+
+}  // namespace dfkv

@@ -1,49 +1,10 @@
-// k_misc.hip -- standalone k_norm/RoPE, hidden_norm, the cos/sin cache builder
-// and a zero-fill kernel.
+// k_misc.hip -- hidden_norm (large-batch path), the cos/sin cache builder and a
+// zero-fill kernel.
 #include <math.h>
 
 #include "dfkv_internal.hpp"
 
 namespace dfkv {
-
-// ---------------------------------------------------------------------------
-// k_norm (or latent norm) + RoPE in place (TensorRT-LLM PR #13995, commits
-// "fuse cross-layer k_norm" and "match RoPE between context and query for
-// YaRN").  One wave per (row, layer, K head) for GQA, per (row, layer) for MLA.
-// ---------------------------------------------------------------------------
-struct NormRopeArgs {
-    NormRopeGeom g;
-    uint16_t *kv;
-    int n_rows;
-};
-
-__global__ __launch_bounds__(256) void k_norm_rope(const NormRopeArgs a) {
-    const NormRopeGeom &g = a.g;
-    uint16_t *kv = a.kv;
-    const int n_rows = a.n_rows;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wv = (int64_t)blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (g.kind == DFKV_GQA) {
-        const int64_t per_row = (int64_t)g.n_layers * g.nkv;
-        if (wv >= (int64_t)n_rows * per_row) return;
-        const int row = (int)(wv / per_row);
-        const int rem = (int)(wv - row * per_row);
-        const int l = rem / g.nkv, h = rem - l * g.nkv;
-        norm_rope_gqa_head(g, kv + (int64_t)row * g.out_dim + (int64_t)l * g.per_layer + h * g.hd, l, row, lane);
-    } else {
-        if (wv >= (int64_t)n_rows * g.n_layers) return;
-        const int row = (int)(wv / g.n_layers);
-        const int l = (int)(wv - (int64_t)row * g.n_layers);
-        norm_rope_mla_layer(g, kv + (int64_t)row * g.out_dim + (int64_t)l * g.per_layer, l, row, lane);
-    }
-}
-
-hipError_t launch_norm_rope(const NormRopeGeom &g, uint16_t *kv, int n_rows, hipStream_t s) {
-    const int64_t waves = (int64_t)n_rows * g.n_layers * (g.kind == DFKV_GQA ? g.nkv : 1);
-    if (waves == 0) return hipSuccess;
-    const int64_t blocks = (waves + 3) / 4;
-    return launch1(k_norm_rope, dim3((unsigned)blocks), dim3(256), s, NormRopeArgs{g, kv, n_rows});
-}
 
 // ---------------------------------------------------------------------------
 // hidden_norm: g[n][:] = bf16(w * f[n][:] / sqrt(mean(f[n]^2) + eps)); one

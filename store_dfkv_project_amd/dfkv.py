@@ -33,7 +33,7 @@ DFKV_MAX_LAYERS = 32
 DFKV_FUSE_NORM_ROPE = 1
 
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
-            "dfkv_rope_cache_build", "dfkv_project", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
+            "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
             "dfkv_store_advance", "dfkv_step")
 
 
@@ -106,6 +106,8 @@ def _load() -> C.CDLL:
         "dfkv_workspace_init": ([P, SZ, P], C.c_int),
         "dfkv_rope_cache_build": ([C.POINTER(dfkv_rope), P, I32, P], C.c_int),
         "dfkv_project": ([gp, wp, P, I64, I32, P, P, I32, P, U32, P, SZ, P], C.c_int),
+        "dfkv_project_fc": ([gp, P, P, P, I64, I32, P, SZ, P], C.c_int),
+        "dfkv_project_kv": ([gp, wp, I32, P, P, I32, P, U32, P, SZ, P], C.c_int),
         "dfkv_norm_rope": ([gp, P, I32, P, P, I32, P, P], C.c_int),
         "dfkv_paged_store": ([gp, P, rp, pp, P, P, P], C.c_int),
         "dfkv_advance": ([gp, rp, op, P], C.c_int),
@@ -241,6 +243,18 @@ def dfkv_project(geom, weights, hidden, hidden_row_stride, n_reqs, ctx_len_in, c
     _check(_lib.dfkv_project(_ref(geom), _ref(weights), _ptr(hidden), int(hidden_row_stride), int(n_reqs),
                              _ptr(ctx_len_in), _ptr(cos_sin), int(cache_len), _ptr(kv_out), int(flags), _ptr(ws),
                              int(ws_bytes), _stream(stream)), "dfkv_project")
+
+
+def dfkv_project_fc(geom, w_fc, w_hnorm, hidden, hidden_row_stride, n_reqs, ws, ws_bytes, stream=None) -> None:
+    _check(_lib.dfkv_project_fc(_ref(geom), _ptr(w_fc), _ptr(w_hnorm), _ptr(hidden), int(hidden_row_stride),
+                                int(n_reqs), _ptr(ws), int(ws_bytes), _stream(stream)), "dfkv_project_fc")
+
+
+def dfkv_project_kv(geom, weights, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out, flags, ws, ws_bytes,
+                    stream=None) -> None:
+    _check(_lib.dfkv_project_kv(_ref(geom), _ref(weights), int(n_reqs), _ptr(ctx_len_in), _ptr(cos_sin),
+                                int(cache_len), _ptr(kv_out), int(flags), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "dfkv_project_kv")
 
 
 def dfkv_norm_rope(geom, w_knorm, n_reqs, ctx_len_in, cos_sin, cache_len, kv, stream=None) -> None:

@@ -131,6 +131,15 @@ class DeviceStep:
                           self.ctx_len, self.cos_sin, self.cache_len, self.kv_out if kv_out is None else kv_out,
                           flags, self.ws, self.ws_bytes, stream)
 
+    def project_fc(self, copy: int = 0, stream=None):
+        w = self.weights[copy]
+        dfkv.dfkv_project_fc(self.gs, w[0], w[1], self.hidden, self.wl.hidden_row_stride, self.wl.n_reqs, self.ws,
+                             self.ws_bytes, stream)
+
+    def project_kv(self, flags: int = dfkv.DFKV_FUSE_NORM_ROPE, copy: int = 0, stream=None):
+        dfkv.dfkv_project_kv(self.gs, self.weight_structs[copy], self.wl.n_reqs, self.ctx_len, self.cos_sin,
+                             self.cache_len, self.kv_out, flags, self.ws, self.ws_bytes, stream)
+
     def norm_rope(self, kv, stream=None):
         dfkv.dfkv_norm_rope(self.gs, self.weights[0][3], self.wl.n_reqs, self.ctx_len, self.cos_sin, self.cache_len,
                             kv, stream)

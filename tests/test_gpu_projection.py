@@ -120,6 +120,12 @@ def test_project_matches_oracle(orc, name, geom, B, rope):
     ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
     torch.cuda.synchronize()
     assert torch.equal(first, ds.kv_out), "projection is not deterministic"
+    # the two stages compose to the whole projection
+    ds.kv_out.fill_(0x7FC0)
+    ds.project_fc()
+    ds.project_kv(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    assert torch.equal(first, ds.kv_out), "dfkv_project_fc + dfkv_project_kv differ from dfkv_project"
 
 
 def test_workspace_shared_across_batch_sizes(orc):
