@@ -9,11 +9,18 @@ resident in HBM before timing starts.
 Timing: 8 consecutive steps rotating over 4 copies of the weights (a copy is
 reused only after 3 other copies, 4 x the weight bytes > the 256 MiB Infinity
 Cache, so every step streams its weights from HBM) are captured in one HIP
-graph, and the graph is replayed back to back between HIP events; a step sits inside the serving loop's own graph, so
-this excludes a per-step graph launch, whose cost is reported separately
+graph, and the graph is replayed back to back between HIP events on its
+stream; a step sits inside the serving loop's own graph, so this excludes a
+per-step graph launch, whose cost is reported separately
 (us_per_step_single_graph_replay).  A spin kernel is queued first so the host
-runs ahead of the GPU.  The dominant kernel (the fc stage, one launch at <= 64
-rows) is timed as 20 back-to-back launches inside one graph.
+runs ahead of the GPU.
+
+Dominant kernel: the fc GEMM (k_stream at <= 64 rows, k_tiled above), timed
+as back-to-back dfkv_project_fc launches inside one graph; the K/V stage
+(dfkv_project_kv) is timed the same way and reported beside it.  At <= 16 rows
+the step is two kernels (fc, then K/V with the finalize, store and advance in
+one launch); the staged path (dfkv_project_fc + dfkv_project_kv +
+dfkv_store_advance) is timed as well for comparison.
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
 """
@@ -47,7 +54,9 @@ def algorithmic(wl, accepted_rows: int) -> dict:
                 step_bytes=w_bytes + x_bytes + accepted_rows * row_bytes,
                 project_bytes=w_bytes + x_bytes + 2 * N * O,
                 fc_bytes=2 * H * K + x_bytes + 2 * N * H + 4 * (H // 16) * N,
-                fc_flops=2.0 * N * K * H, flops=2.0 * N * (K * H + H * O))
+                fc_flops=2.0 * N * K * H, flops=2.0 * N * (K * H + H * O),
+                kv_bytes=2 * (O * H + H + g.n_layers * g.knorm_dim) + 2 * N * H + 2 * N * O,
+                kv_flops=2.0 * N * H * O)
 
 
 def cpu_baseline(wl, seconds: float) -> dict:
@@ -133,36 +142,39 @@ def main() -> int:
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
 
-    # Graphs.  A decode step sits inside the serving loop's own captured graph, so the step is timed
-    # as R consecutive steps captured in one graph (one per weight copy: no step finds its weights in
-    # the Infinity Cache), replayed back to back; the per-replay launch cost of a graph holding a
-    # single step is reported next to it.  The dominant kernel (the fc stage) is timed as
-    # FC_PER_GRAPH back-to-back launches in one graph, so its events bracket kernels only.
+    # Graphs (see the module docstring).
     FC_PER_GRAPH = 5 * R
     STEPS_PER_GRAPH = 2 * R
+    small = wl.n_rows <= 16
     with torch.cuda.stream(stream):
         for c in range(R):       # eager warm-up of every path before capture
             ds.step(copy=c)
             ds.project_fc(copy=c)
+            ds.project_kv(copy=c)
     torch.cuda.synchronize()
-    g_steps = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_steps, stream=stream):
-        for i in range(STEPS_PER_GRAPH):
-            ds.step(copy=i % R)
+
+    def capture(fn, n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(n):
+                fn(i % R)
+        return g
+
+    def staged(c):
+        ds.project_fc(copy=c)
+        ds.project_kv(copy=c)
+        ds.store_advance()
+
+    g_steps = capture(lambda c: ds.step(copy=c), STEPS_PER_GRAPH)
     g_single = []
     for c in range(R):
         g1 = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g1, stream=stream):
             ds.step(copy=c)
         g_single.append(g1)
-    g_fc = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_fc, stream=stream):
-        for i in range(FC_PER_GRAPH):
-            ds.project_fc(copy=i % R)
-    g_proj = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_proj, stream=stream):
-        for c in range(R):
-            ds.project(copy=c)
+    g_fc = capture(lambda c: ds.project_fc(copy=c), FC_PER_GRAPH)
+    g_kv = capture(lambda c: ds.project_kv(copy=c), FC_PER_GRAPH)
+    g_staged = capture(staged, STEPS_PER_GRAPH) if small else None
     torch.cuda.synchronize()
     accepted = int(ds.write_mask.sum().item())
 
@@ -188,36 +200,36 @@ def main() -> int:
     wall = time.perf_counter() - t_wall0
     single_us = timed(g_single, args.steps, args.warmup, 1)
     fc_us = timed([g_fc], max(1, args.steps // FC_PER_GRAPH * 4), 2, FC_PER_GRAPH)
-    proj_us = timed([g_proj], max(1, args.steps // R), max(1, args.warmup // R), R)
-    step_avg_us = float(step_us.mean())
+    kv_us = timed([g_kv], max(1, args.steps // FC_PER_GRAPH * 4), 2, FC_PER_GRAPH)
+    staged_us = timed([g_staged], n_rep, 1, STEPS_PER_GRAPH) if small else None
 
     alg = algorithmic(wl, accepted)
-    us_step = float(step_avg_us)
+    us_step = float(step_us.mean())
     fc_mean = float(fc_us.mean())
-    proj_mean = float(proj_us.mean())
-    small = wl.n_rows <= 64
-    if small:
+    kv_mean = float(kv_us.mean())
+    if wl.n_rows <= 64:
         achieved = alg["fc_bytes"] / (fc_mean * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4))
-        kname = "k_stream<fc> (dfkv_project_fc: fc GEMM streaming w_fc, f + row statistics)"
+                    frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                    kernel="k_stream<fc> (dfkv_project_fc: the fc GEMM streaming w_fc, f + row statistics)",
+                    algorithmic_bytes_per_launch=alg["fc_bytes"])
     else:
         achieved = alg["fc_flops"] / (fc_mean * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4))
-        kname = "k_tiled (dfkv_project_fc: fc GEMM) + k_hidden_norm"
-    proj_gbs = alg["project_bytes"] / (proj_mean * 1e-6) / 1e9
-    roof.update(traffic=None, kernel=kname, algorithmic_bytes_per_launch=alg["fc_bytes"],
-                algorithmic_flops_per_launch=alg["fc_flops"], launch_us_mean=round(fc_mean, 2),
-                launch_us_p10=round(float(np.percentile(fc_us, 10)), 2),
-                launch_us_p90=round(float(np.percentile(fc_us, 90)), 2),
-                projection={"us_mean": round(proj_mean, 2), "algorithmic_bytes": alg["project_bytes"],
-                            "flops": alg["flops"], "GB/s": round(proj_gbs, 1),
-                            "hbm_frac": round(proj_gbs / HBM_PEAK_GBS, 4),
-                            "TFLOP/s": round(alg["flops"] / (proj_mean * 1e-6) / 1e12, 2)},
-                step={"us_mean": round(us_step, 2), "algorithmic_bytes": alg["step_bytes"],
-                      "GB/s": round(alg["step_bytes"] / (us_step * 1e-6) / 1e9, 1),
-                      "TFLOP/s": round(alg["flops"] / (us_step * 1e-6) / 1e12, 2)})
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
+                    kernel="k_tiled (dfkv_project_fc: the fc GEMM) + k_hidden_norm",
+                    algorithmic_flops_per_launch=alg["fc_flops"])
+    roof.update(launch_us_mean=round(fc_mean, 2), launch_us_p10=round(float(np.percentile(fc_us, 10)), 2),
+                launch_us_p90=round(float(np.percentile(fc_us, 90)), 2))
+    roof["kv_stage"] = {"us_mean": round(kv_mean, 2), "algorithmic_bytes": alg["kv_bytes"],
+                        "GB/s": round(alg["kv_bytes"] / (kv_mean * 1e-6) / 1e9, 1),
+                        "TFLOP/s": round(alg["kv_flops"] / (kv_mean * 1e-6) / 1e12, 2)}
+    roof["step"] = {"us_mean": round(us_step, 2), "algorithmic_bytes": alg["step_bytes"],
+                    "GB/s": round(alg["step_bytes"] / (us_step * 1e-6) / 1e9, 1),
+                    "hbm_frac": round(alg["step_bytes"] / (us_step * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                    "TFLOP/s": round(alg["flops"] / (us_step * 1e-6) / 1e12, 2)}
+    if staged_us is not None:
+        roof["staged_path_us_per_step"] = round(float(staged_us.mean()), 2)
 
     out = {
         "metric": METRIC,

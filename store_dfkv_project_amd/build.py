@@ -20,18 +20,19 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libdfkv needs the ROCm toolchain")
 
 
-def command(out: str = LIB) -> list:
+def command(out: str = LIB, defines=()) -> list:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+            *[f"-D{d}" for d in defines],
             # packed fp32 instructions are kept out of every kernel (hipcc's host pass
             # warns that it does not know the feature; that is expected)
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wno-unused-result", *srcs, "-o", out]
 
 
-def build(out: str = LIB, verbose: bool = False) -> str:
+def build(out: str = LIB, verbose: bool = False, defines=()) -> str:
     tmp = out + ".tmp"
-    cmd = command(tmp)
+    cmd = command(tmp, defines)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)

@@ -75,12 +75,45 @@ int choose_kv_splits(int tiles, int kblocks, int64_t M) {
     return best > 0 ? best : kblocks;
 }
 
+// The small-batch K/V kernel's groups: S splits of the K/V GEMM, each a multiple of 8 k-blocks
+// (every wave takes the same number of blocks of every tile) whose g fits the LDS stage, times
+// groups of ntg consecutive 16-feature tiles (ntg <= the tiles of one unit, so a group touches at
+// most two units).  Picks the largest group count that fits the resident workgroup slots (one wave
+// of groups, all of equal size), preferring fewer splits on ties.  False when no split qualifies.
+bool choose_kv_groups(const dfkv_geom *g, int64_t M, int *S_out, int *ntg_out) {
+    const int kb = g->hidden / 128;
+    const int T = (int)(out_dim(g) / 16);
+    const int tpu = (g->kind == DFKV_GQA ? g->head_dim : per_layer(g)) / 16;
+    int best_n = 0, best_S = 0, best_ntg = 0;
+    for (int S = 1; S <= kb; ++S) {
+        if (kb % S || (kb / S) % 8 || !stage_fits(M, kb / S)) continue;
+        for (int ntg = 1; ntg <= tpu && ntg <= T; ++ntg) {
+            if (T % ntg) continue;
+            const int n = S * (T / ntg);
+            const bool better = best_n == 0 ? true
+                                : (n <= kKvSlots ? (best_n > kKvSlots || n > best_n) : (best_n > kKvSlots && n < best_n));
+            if (better) {
+                best_n = n;
+                best_S = S;
+                best_ntg = ntg;
+            }
+        }
+    }
+    if (best_n == 0) return false;
+    *S_out = best_S;
+    *ntg_out = best_ntg;
+    return true;
+}
+
 struct Plan {
     int64_t M;
     bool skinny;
+    bool kvfin;  // k_kvgroups + k_kvfinal run the K/V stage
     int S_kv;
-    // f [M][H]; small batch: ss [H/16][M] and K/V partials [S][M][O]; large batch: g [M][H]
-    size_t off_f, off_g, off_ss, off_part, total;
+    int ntg;     // k_kvfin: tiles per K/V group
+    // bookkeeping area of the small-batch K/V kernels; f [M][H]; small batch: ss [H/16][M] and K/V
+    // partials [S][M][O]; large batch: g [M][H]
+    size_t off_book, off_f, off_g, off_ss, off_part, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -97,10 +130,12 @@ dfkv_status make_plan(const dfkv_geom *g, int32_t n_reqs, Plan *pl) {
     p.skinny = M <= kSkinnyMaxRows;
     const size_t Mp = M > 0 ? (size_t)M : 1;
     size_t off = 0;
+    p.off_book = off; off = up256(off + kv_book_bytes(g->rope_dim));
     p.off_f = off; off = up256(off + Mp * H * 2);
     p.off_g = off; off = up256(off + Mp * H * 2);
+    p.kvfin = M >= 1 && M <= kKvMaxRows && choose_kv_groups(g, M, &p.S_kv, &p.ntg);
     if (p.skinny) {
-        p.S_kv = choose_kv_splits((int)(O / 16), (int)(H / 128), M);
+        if (!p.kvfin) p.S_kv = choose_kv_splits((int)(O / 16), (int)(H / 128), M);
         p.off_ss = off;   off = up256(off + (size_t)(H / 16) * Mp * 4);
         p.off_part = off; off = up256(off + (size_t)p.S_kv * Mp * O * 4);
     } else {
@@ -366,6 +401,10 @@ dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int
     return hip_status(launch_hidden_norm(f, (const uint16_t *)w_hnorm, gb, (int)pl.M, (int)H, g->eps, s));
 }
 
+dfkv_status run_kvfin(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx, const float *cs,
+                      int32_t cache_len, void *kv_out, bool fuse, void *ws, const Plan &pl, FinalizeParams fin,
+                      hipStream_t s);
+
 dfkv_status run_kv(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx, const float *cs, int32_t cache_len,
                    void *kv_out, bool fuse, void *ws, const Plan &pl, FinalizeParams fin, bool need_finalize,
                    hipStream_t s) {
@@ -373,6 +412,7 @@ dfkv_status run_kv(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx
     char *wsb = (char *)ws;
     const int64_t H = g->hidden, O = out_dim(g);
     hipError_t e;
+    if (pl.kvfin) return run_kvfin(g, w, ctx, cs, cache_len, kv_out, fuse, ws, pl, fin, s);
     fin.nr = nr_geom(g, w->w_knorm, ctx, cs, cache_len);
     fin.norm = fuse ? 1 : 0;
     fin.kv_out = (uint16_t *)kv_out;
@@ -411,9 +451,51 @@ dfkv_status run_kv(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx
     return hip_status(launch_finalize(fin, s));
 }
 
+// The K/V stage at <= 16 rows (k_kvgroups then k_kvfinal): hidden_norm, the K/V GEMM, k_norm/RoPE
+// into kv_out and, when `fin` asks for them, the paged store and the advance; on f and its
+// statistics left in ws by the fc stage.
+dfkv_status run_kvfin(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx, const float *cs,
+                      int32_t cache_len, void *kv_out, bool fuse, void *ws, const Plan &pl, FinalizeParams fin,
+                      hipStream_t s) {
+    char *wsb = (char *)ws;
+    const int64_t H = g->hidden, O = out_dim(g);
+    KvParams kp;
+    memset(&kp, 0, sizeof kp);
+    kp.kv.w = (const uint16_t *)w->w_kv;
+    kp.kv.x = (const uint16_t *)(wsb + pl.off_f);
+    kp.kv.ldx = H;
+    kp.kv.M = (int32_t)pl.M;
+    kp.kv.K = (int32_t)H;
+    kp.kv.O = (int32_t)O;
+    kp.kv.S = pl.S_kv;
+    kp.kv.nbs = (int32_t)(H / 128 / pl.S_kv);
+    kp.kv.part = (float *)(wsb + pl.off_part);
+    kp.kv.w_hn = (const uint16_t *)w->w_hnorm;
+    kp.kv.ss_in = (const float *)(wsb + pl.off_ss);
+    kp.kv.T_in = (int32_t)(H / 16);
+    kp.kv.eps = g->eps;
+    fin.nr = nr_geom(g, w->w_knorm, ctx, cs, cache_len);
+    fin.norm = fuse ? 1 : 0;
+    fin.kv_out = (uint16_t *)kv_out;
+    fin.part = kp.kv.part;
+    fin.S = pl.S_kv;
+    fin.M = (int32_t)pl.M;
+    fin.src = nullptr;
+    // the kernel reads the pre-step ctx_len once, for RoPE and for the bookkeeping alike
+    if ((fin.store || fin.advance) && fin.ctx_len != ctx) return DFKV_ERR_SHAPE;
+    kp.fin = fin;
+    kp.book = wsb + pl.off_book;
+    kp.ntg = pl.ntg;
+    kp.n_groups = (int32_t)(O / 16 / pl.ntg) * pl.S_kv;
+    kp.unit_cols = g->kind == DFKV_GQA ? g->head_dim : per_layer(g);
+    kp.n_units = (int32_t)(O / kp.unit_cols);
+    return hip_status(launch_kv(kp, s));
+}
+
 dfkv_status run_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t ld, const int32_t *ctx,
                         const float *cs, int32_t cache_len, void *kv_out, bool fuse, void *ws, const Plan &pl,
                         const FinalizeParams &fin, bool need_finalize, hipStream_t s) {
+    if (pl.M == 0) return DFKV_OK;
     dfkv_status st = run_fc(g, w->w_fc, hidden, ld, w->w_hnorm, ws, pl, s);
     if (st != DFKV_OK) return st;
     return run_kv(g, w, ctx, cs, cache_len, kv_out, fuse, ws, pl, fin, need_finalize, s);

@@ -132,6 +132,26 @@ struct StreamParams {
 };
 hipError_t launch_stream(const StreamParams &p, hipStream_t s);
 
+// K/V stage of the small-batch step (M <= 16 rows): hidden_norm + the stacked K/V GEMM as split-K
+// groups (k_kvgroups), then the finalize (k_kvfinal) -- k_kvfin.hip.
+constexpr int kKvMaxRows = 16;
+constexpr int kKvSlots = 512;    // resident workgroups of k_kvgroups: 2 per CU x 256 CUs
+// Row/request bookkeeping left in the workspace by k_kvgroups for k_kvfinal (byte offsets):
+// slot int64 [16], ctx / ctx_new / bonus int32 [16] each, then the rows' cos/sin values fp32 [16][rot].
+constexpr int kKvBookCtx = 128, kKvBookCtxNew = 192, kKvBookBonus = 256, kKvBookCs = 384;
+struct KvParams {
+    StreamParams kv;          // the K/V GEMM: kv.S splits of kv.nbs k-blocks, g staged in LDS
+    FinalizeParams fin;       // k_norm/RoPE, store, advance
+    void *book;               // bookkeeping area of the workspace
+    int32_t n_groups;         // kv.S splits x (O/16/ntg) tile groups
+    int32_t ntg;              // tiles per group
+    int32_t unit_cols;        // output columns per unit (head_dim for GQA, latent + rope for MLA)
+    int32_t n_units;          // O / unit_cols
+    int32_t lds_wk, lds_cs;   // byte offsets in k_kvfinal's dynamic LDS (set by launch_kv)
+};
+hipError_t launch_kv(const KvParams &p, hipStream_t s);
+size_t kv_book_bytes(int rot);
+
 // Tiled MFMA GEMM for larger M: out[n][o] = bf16(sum_k x[n][k] w[o][k]).
 struct TiledParams {
     const uint16_t *x;

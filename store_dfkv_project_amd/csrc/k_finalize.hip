@@ -23,55 +23,13 @@
 // part of MLA rotated only; V passes through.  The result goes to kv_out
 // and, when the row's write predicate holds, to the layer's pool.  Rows whose
 // predicate fails never touch the pools.
-#include "dfkv_internal.hpp"
+#include "finalize_common.hpp"
 
 namespace dfkv {
 
-// Write predicate and slot of token i of request r (row = r*W + i).  The request's
-// fields are loaded together; only the block-table entry depends on them.
-__device__ __forceinline__ bool row_destination(const FinalizeParams &p, int r, int i, int row, int64_t &slot) {
-    const uint8_t d = p.dummy[r];
-    const int32_t n = p.n_acc[r];
-    const int32_t c = p.ctx_len[r];
-    const int32_t lim = p.limit[r];
-    const uint8_t rv = p.row_valid ? p.row_valid[row] : (uint8_t)1;
-    slot = -1;
-    const int64_t pos = (int64_t)c + i;
-    if (d || !(i < n) || !rv || pos < 0 || pos >= (int64_t)lim) return false;
-    const int64_t pidx = pos / p.pg;
-    if (pidx >= p.bt_cols) return false;
-    const int32_t page = p.bt[(int64_t)r * p.bt_stride + pidx];
-    if (page < 0 || page >= p.num_pages) return false;
-    slot = (int64_t)page * p.pg + (pos - pidx * p.pg);
-    return true;
-}
-
-__device__ __forceinline__ void request_advance(const FinalizeParams &p, int r) {
-    const int32_t c = p.ctx_len[r], n = p.n_acc[r], lim = p.limit[r];
-    const bool d = p.dummy[r] != 0;
-    const int64_t adv = (int64_t)c + n;
-    const int32_t ctx_new = d ? 0 : (int32_t)(adv < (int64_t)lim ? adv : (int64_t)lim);
-    const int nb = n < 1 ? 1 : (n > p.W ? p.W : n);
-    const int32_t bonus = p.acc[(int64_t)r * p.acc_sr + (int64_t)(nb - 1) * p.acc_st];
-    for (int j = threadIdx.x; j < p.bs_blk; j += blockDim.x) {
-        p.emb[(int64_t)r * p.bs_blk + j] = j == 0 ? bonus : p.mask_id;
-        p.q_pos[(int64_t)r * p.bs_blk + j] = ctx_new + j;
-    }
-    for (int j = threadIdx.x; j < p.W; j += blockDim.x) p.c_pos[(int64_t)r * p.W + j] = (int32_t)((int64_t)c + j);
-    if (threadIdx.x == 0) {
-        p.bonus[r] = bonus;
-        p.ctx_out[r] = ctx_new;
-        p.seq_len[r] = ctx_new + p.bs_blk;
-    }
-}
-
 // one element of the row's stacked projection, as fp32 (the bf16-rounded GEMM output)
 __device__ __forceinline__ float load_y(const FinalizeParams &p, int row, int64_t col) {
-    if (p.part) {
-        float y = 0.f;
-        for (int s = 0; s < p.S; ++s) y += p.part[((int64_t)s * p.M + row) * p.O + col];
-        return bf2f(f2bf(y));
-    }
+    if (p.part) return part_y(p.part, p.S, p.M, p.O, row, col);
     return bf2f(p.src[(int64_t)row * p.O + col]);
 }
 
@@ -116,11 +74,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
             p.wmask[row] = w ? 1 : 0;
         }
         if (!out && !w) return;
-        int64_t dst0 = 0;
-        if (w) {
-            const int64_t page = slot / p.pg;
-            dst0 = page * p.sp + (slot - page * p.pg) * p.ss;
-        }
+        const int64_t dst0 = w ? slot_offset(p, slot) : 0;
         const int nch = p.per_layer >> 3;
         for (int c = tid; c < nch; c += kFinThreads) {
             const int e = c << 3;
@@ -167,11 +121,7 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
             p.slot[row] = slot;
             p.wmask[row] = w ? 1 : 0;
         }
-        int64_t dst0 = 0;
-        if (w) {
-            const int64_t page = slot / p.pg;
-            dst0 = page * p.sp + (slot - page * p.pg) * p.ss;
-        }
+        const int64_t dst0 = w ? slot_offset(p, slot) : 0;
         // 3. V straight through
         for (int c = tid; c < vch; c += kFinThreads) {
             const u32x4 v = c == tid ? vv : load_y8(p, row, lay + kvh + (c << 3));
@@ -194,27 +144,20 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
                     }
                 }
             }
-            float ss = 0.f;
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) ss += a[q2] * a[q2] + b[q2] * b[q2];
-            ss = wave_sum(ss);
-            const float rinv = 1.0f / sqrtf(ss / (float)hd + p.nr.eps);
+            uint16_t ka[2], kb[2];
+            knorm_rope_head(a, b, hd, p.nr.eps, wk, cs, lane, ka, kb);
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
                 const int j = lane + q2 * 64;
                 if (j < half) {
-                    const float ua = bf2f(f2bf(bf2f(wk[j]) * (a[q2] * rinv)));
-                    const float ub = bf2f(f2bf(bf2f(wk[j + half]) * (b[q2] * rinv)));
-                    const float c = cs[j], sn = cs[half + j];
-                    const uint16_t ka = f2bf(ua * c - ub * sn), kb = f2bf(ub * c + ua * sn);
                     if (out) {
-                        out[h * hd + j] = ka;
-                        out[h * hd + j + half] = kb;
+                        out[h * hd + j] = ka[q2];
+                        out[h * hd + j + half] = kb[q2];
                     }
                     if (w) {
                         uint16_t *d = p.pk[l] + dst0 + (int64_t)h * p.sh;
-                        d[j] = ka;
-                        d[j + half] = kb;
+                        d[j] = ka[q2];
+                        d[j + half] = kb[q2];
                     }
                 }
             }
@@ -240,22 +183,14 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
             p.slot[row] = slot;
             p.wmask[row] = w ? 1 : 0;
         }
-        uint16_t *d = nullptr;
-        if (w) {
-            const int64_t page = slot / p.pg;
-            d = p.pk[l] + page * p.sp + (slot - page * p.pg) * p.ss;
-        }
-        float ss = 0.f;
-#pragma unroll
-        for (int q2 = 0; q2 < 16; ++q2) ss += v[q2] * v[q2];
-        ss = wave_sum(ss);
-        const float rinv = 1.0f / sqrtf(ss / (float)R + p.nr.eps);
+        uint16_t *d = w ? p.pk[l] + slot_offset(p, slot) : nullptr;
+        const float rinv = latent_rinv(v, R, p.nr.eps);
         const uint16_t *wk = p.nr.w_knorm + (int64_t)l * R;
 #pragma unroll
         for (int q2 = 0; q2 < 16; ++q2) {
             const int e = lane + q2 * 64;
             if (e < R) {
-                const uint16_t o = f2bf(bf2f(wk[e]) * (v[q2] * rinv));
+                const uint16_t o = latent_elem(wk[e], v[q2], rinv);
                 if (out) out[e] = o;
                 if (d) d[e] = o;
             }
@@ -263,7 +198,8 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
         if (lane < half) {
             const float *cs = rope_row(p.nr, row);
             const float c = cs[lane], sn = cs[half + lane];
-            const uint16_t ka = f2bf(ra * c - rb * sn), kb = f2bf(rb * c + ra * sn);
+            uint16_t ka, kb;
+            rope_pair(ra, rb, c, sn, ka, kb);
             if (out) {
                 out[R + lane] = ka;
                 out[R + lane + half] = kb;

@@ -1,0 +1,434 @@
+// k_kvfin.hip -- the K/V stage of the small-batch step (M = B*W <= 16 token
+// rows) in two launches: hidden_norm + the stacked K/V GEMM as split-K groups
+// (k_kvgroups), then k_norm / RoPE, kv_out, the paged store into every layer's
+// pool and the per-request advance (k_kvfinal).
+//
+// Sources (page titles and sections): TensorRT-LLM PR #20550 "fuse the
+// decode-step drafter bookkeeping into Triton kernels", sections
+// TLLM_DFLASH_OVERLAP_CONTEXT_PROJECTION (fc + hidden_norm + latent GEMM +
+// RMSNorm/RoPE) and TLLM_DFLASH_FUSED_PROLOGUE (mask, clamp, page lookup, write
+// to every layer, advance); TensorRT-LLM PR #13995 "DFlash performance
+// optimizations" (one GEMM stacked across layers; fused cross-layer k_norm; one
+// cos/sin cache for context and query).
+//
+// Input: f = bf16(hidden . w_fc^T) and its per-16-column sums of squares, left in
+// the workspace by the fc kernel (k_stream) that runs before these.
+//
+// k_kvgroups: S splits of the K/V GEMM's k range times groups of ntg consecutive
+// 16-feature tiles; one workgroup per (split, group), all of them resident at
+// once (the group count is chosen to fit the chip's workgroup slots), each with
+// the same amount of weights to stream.  A group stages g = hidden_norm(f) for
+// its split in LDS once, streams its tiles' weights through a ring of
+// registers, and writes each tile's fp32 partial sums.  Group 0 also gathers,
+// while it streams, everything the finalize needs of the rows and requests
+// (destination slot, cos/sin values, advance outputs) into the workspace, so
+// that no dependent load sits on the step's tail.
+//
+// k_kvfinal: one workgroup per unit -- a GQA K or V head, or an MLA layer's
+// latent + rope: one round of loads (the unit's split partials, its k_norm
+// weights, the rows' cos/sin values and slots), then the per-head arithmetic of
+// finalize_common.hpp into kv_out and the pools; workgroup 0 also writes the
+// bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
+// inside the GEMM kernel by the last arriving group: there every dependent hop
+// (store drain, arrival atomic, partial loads) waited behind the weight stream.
+#include "finalize_common.hpp"
+
+namespace dfkv {
+
+constexpr int kKvWaves = 8;
+constexpr int kKvThreads = kKvWaves * 64;
+// Tuning (overridable when building): weight k-blocks in flight per wave, and waves per SIMD
+// (4: <= 128 VGPRs, two workgroups per CU).
+#ifndef DFKV_KV_RING
+#define DFKV_KV_RING 3
+#endif
+#ifndef DFKV_KV_WPE
+#define DFKV_KV_WPE 4
+#endif
+constexpr int kKvRing = DFKV_KV_RING;
+constexpr int kKvWPE = DFKV_KV_WPE;
+
+// Row and request bookkeeping group 0 leaves in the workspace for the finalize kernel.
+__device__ __forceinline__ int64_t *book_slot(void *b) { return (int64_t *)b; }
+__device__ __forceinline__ int32_t *book_ctx(void *b) { return (int32_t *)((char *)b + kKvBookCtx); }
+__device__ __forceinline__ int32_t *book_ctx_new(void *b) { return (int32_t *)((char *)b + kKvBookCtxNew); }
+__device__ __forceinline__ int32_t *book_bonus(void *b) { return (int32_t *)((char *)b + kKvBookBonus); }
+__device__ __forceinline__ float *book_cs(void *b) { return (float *)((char *)b + kKvBookCs); }
+
+// ---------------------------------------------------------------------------
+// k_kvfinal: one workgroup per unit
+// ---------------------------------------------------------------------------
+
+// Unit u for every row: a GQA K or V head (columns [u*hd, (u+1)*hd)) or an MLA layer (latent +
+// rope).  Phase A (all threads, one round of loads): the unit's split partials summed in split order
+// and rounded to bf16, its k_norm weights, the rows' cos/sin values and slots, into LDS.  Phase B:
+// one wave per row, the per-head arithmetic of finalize_common.hpp, into kv_out and the pools.
+__global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
+    extern __shared__ __attribute__((aligned(16))) uint16_t sh_dyn[];
+    const FinalizeParams &p = kp.fin;
+    const int u = blockIdx.x;
+    const int M = p.M, O = p.O, S = p.S;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int cols = kp.unit_cols;
+    const bool gqa = p.kind == DFKV_GQA;
+    const int l = gqa ? u / (2 * p.nkv) : u;
+    const int rem = gqa ? u - l * 2 * p.nkv : 0;
+    const bool is_v = gqa && rem >= p.nkv;
+    const int h = is_v ? rem - p.nkv : rem;
+    const int64_t col0 = gqa ? (int64_t)u * cols : (int64_t)l * p.per_layer;
+    const bool norm = p.norm && !is_v;
+    const int rot = p.nr.rope_dim;
+    const int nwk = gqa ? cols : p.nr.latent;
+    void *book = kp.book;
+
+    uint16_t *y = sh_dyn;                                        // [M][cols] bf16
+    uint16_t *wk = (uint16_t *)((char *)sh_dyn + kp.lds_wk);     // [cols]
+    float *cs = (float *)((char *)sh_dyn + kp.lds_cs);           // [M][rot]
+    __shared__ int64_t sh_slot[kKvMaxRows];
+
+    // phase A
+    constexpr int EB = 2;   // elements per thread per round
+    constexpr int SB = 8;   // splits per round
+    const int total = M * cols;
+    for (int e0 = tid; e0 < total; e0 += EB * kKvThreads) {
+        float acc[EB] = {0.f, 0.f};
+        for (int s0 = 0; s0 < S; s0 += SB) {
+            float v[EB][SB];
+#pragma unroll
+            for (int i = 0; i < EB; ++i) {
+                const int e = e0 + i * kKvThreads;
+                const int n = e / cols, c = e - (e / cols) * cols;
+#pragma unroll
+                for (int k = 0; k < SB; ++k)
+                    v[i][k] = (e < total && s0 + k < S) ? p.part[((int64_t)(s0 + k) * M + n) * O + col0 + c] : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < EB; ++i)
+#pragma unroll
+                for (int k = 0; k < SB; ++k)
+                    if (s0 + k < S) acc[i] += v[i][k];
+        }
+#pragma unroll
+        for (int i = 0; i < EB; ++i) {
+            const int e = e0 + i * kKvThreads;
+            if (e < total) y[e] = f2bf(acc[i]);
+        }
+    }
+    if (norm) {
+        const uint16_t *w = p.nr.w_knorm + (int64_t)l * nwk;
+        for (int c = tid; c < nwk; c += kKvThreads) wk[c] = w[c];
+        const float *bcs = book_cs(book);
+        for (int e = tid; e < M * rot; e += kKvThreads) cs[e] = bcs[e];
+    }
+    if (tid < M) sh_slot[tid] = p.store ? book_slot(book)[tid] : -1;
+    __syncthreads();
+
+    // phase B
+    if (gqa) {
+        const int hd = cols, half = hd >> 1;
+        uint16_t *pool = is_v ? p.pv[l] : p.pk[l];
+        for (int n = wave; n < M; n += kKvWaves) {
+            float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int j = lane + q2 * 64;
+                if (j < half) {
+                    a[q2] = bf2f(y[n * hd + j]);
+                    b[q2] = bf2f(y[n * hd + j + half]);
+                }
+            }
+            uint16_t ka[2], kb[2];
+            if (norm) {
+                knorm_rope_head(a, b, hd, p.nr.eps, wk, cs + n * rot, lane, ka, kb);
+            } else {
+#pragma unroll
+                for (int q2 = 0; q2 < 2; ++q2) {
+                    ka[q2] = f2bf(a[q2]);
+                    kb[q2] = f2bf(b[q2]);
+                }
+            }
+            const int64_t slot = sh_slot[n];
+            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)n * O + col0 : nullptr;
+            uint16_t *d = slot >= 0 ? pool + slot_offset(p, slot) + (int64_t)h * p.sh : nullptr;
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int j = lane + q2 * 64;
+                if (j < half) {
+                    if (out) {
+                        out[j] = ka[q2];
+                        out[j + half] = kb[q2];
+                    }
+                    if (d) {
+                        d[j] = ka[q2];
+                        d[j + half] = kb[q2];
+                    }
+                }
+            }
+        }
+    } else {
+        const int R = p.nr.latent, half = rot >> 1;
+        for (int n = wave; n < M; n += kKvWaves) {
+            float v[16];
+#pragma unroll
+            for (int q2 = 0; q2 < 16; ++q2) {
+                const int e = lane + q2 * 64;
+                v[q2] = e < R ? bf2f(y[n * cols + e]) : 0.f;
+            }
+            float ra = 0.f, rb = 0.f;
+            if (lane < half) {
+                ra = bf2f(y[n * cols + R + lane]);
+                rb = bf2f(y[n * cols + R + lane + half]);
+            }
+            const int64_t slot = sh_slot[n];
+            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)n * O + col0 : nullptr;
+            uint16_t *d = slot >= 0 ? p.pk[l] + slot_offset(p, slot) : nullptr;
+            const float rinv = norm ? latent_rinv(v, R, p.nr.eps) : 1.f;
+#pragma unroll
+            for (int q2 = 0; q2 < 16; ++q2) {
+                const int e = lane + q2 * 64;
+                if (e < R) {
+                    const uint16_t o = norm ? latent_elem(wk[e], v[q2], rinv) : f2bf(v[q2]);
+                    if (out) out[e] = o;
+                    if (d) d[e] = o;
+                }
+            }
+            if (lane < half) {
+                uint16_t ka = f2bf(ra), kb = f2bf(rb);
+                if (norm) {
+                    const float *c = cs + n * rot;
+                    rope_pair(ra, rb, c[lane], c[half + lane], ka, kb);
+                }
+                if (out) {
+                    out[R + lane] = ka;
+                    out[R + lane + half] = kb;
+                }
+                if (d) {
+                    d[R + lane] = ka;
+                    d[R + lane + half] = kb;
+                }
+            }
+        }
+    }
+
+    // workgroup 0: the bookkeeping outputs (slot, write mask, context positions; bonus, embedding
+    // ids, query positions, advanced ctx_len, seq_len)
+    if (u != 0) return;
+    if (p.store && tid < M) {
+        p.slot[tid] = sh_slot[tid];
+        p.wmask[tid] = sh_slot[tid] >= 0 ? 1 : 0;
+    }
+    if (!p.advance) return;
+    const int32_t *ctx = book_ctx(book), *ctx_new = book_ctx_new(book), *bonus = book_bonus(book);
+    for (int e = tid; e < M; e += kKvThreads) {
+        const int r = e / p.W, i = e - (e / p.W) * p.W;
+        p.c_pos[e] = (int32_t)((int64_t)ctx[r] + i);
+    }
+    for (int e = tid; e < p.B * p.bs_blk; e += kKvThreads) {
+        const int r = e / p.bs_blk, j = e - (e / p.bs_blk) * p.bs_blk;
+        p.emb[e] = j == 0 ? bonus[r] : p.mask_id;
+        p.q_pos[e] = ctx_new[r] + j;
+    }
+    if (tid < p.B) {
+        p.bonus[tid] = bonus[tid];
+        p.ctx_out[tid] = ctx_new[tid];
+        p.seq_len[tid] = ctx_new[tid] + p.bs_blk;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_kvgroups: one workgroup per (split, tile group)
+// ---------------------------------------------------------------------------
+
+// Group (s, t0): split s of the K/V GEMM (k-blocks [s*nbs, (s+1)*nbs), nbs a multiple of the wave
+// count, so every wave takes nbs/8 blocks of every tile) over tiles [t0, t0 + ntg).  Same per-tile
+// arithmetic as the staged K/V GEMM of stream_core.hpp: waves interleave the split's blocks, their
+// sums are added in wave order.
+__global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvWPE, 8))) void k_kvgroups(
+    const KvParams kp) {
+    constexpr int D = kKvRing;
+    constexpr int WAVES = kKvWaves, NT = kKvThreads, NP = 17;
+    __shared__ float red[2 * kKvWaves * 16 * 17];
+    __shared__ float sh_rinv[16];
+    extern __shared__ __attribute__((aligned(16))) uint16_t sh_g[];  // g [M][kc + 8]
+    const StreamParams &p = kp.kv;
+    const FinalizeParams &fin = kp.fin;
+    const int groups = kp.n_groups / p.S;
+    const int s = blockIdx.x / groups, t0 = (blockIdx.x - s * groups) * kp.ntg;
+    const bool book = blockIdx.x == 0;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
+    const int M = p.M, ntg = kp.ntg;
+    const int kb0 = s * p.nbs, kc = p.nbs * 128, ldg = kc + 8;
+    const int nbw = p.nbs / WAVES;      // blocks per wave per tile (the same for every wave)
+    const int total = ntg * nbw;        // this wave's blocks over the group
+
+    u32x4 a[D][4];
+    auto load = [&](int slot, int f) {
+        const int i = f / nbw, j = f - (f / nbw) * nbw;
+        const uint16_t *wrow = p.w + (int64_t)((t0 + i) * 16 + c16) * p.K;
+        const int64_t k = (int64_t)(kb0 + wave + j * WAVES) * 128;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wrow + k + (u * 4 + q) * 8);
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < total) load(d, d);
+
+    // Staging hop: f, w_hn and the row statistics for g; in group 0, with them, the rows' and
+    // requests' fields (wave 0 lanes: row tid; wave 1 lanes: request tid - 64).
+    const int c8n = kc >> 3;
+    u32x4 fv[kStageChunks], wv[kStageChunks];
+#pragma unroll
+    for (int i = 0; i < kStageChunks; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < M * c8n) {
+            const int n = idx / c8n, c8 = idx - (idx / c8n) * c8n;
+            const int64_t kk = (int64_t)kb0 * 128 + (c8 << 3);
+            fv[i] = *(const u32x4 *)(p.x + (int64_t)n * p.ldx + kk);
+            wv[i] = *(const u32x4 *)(p.w_hn + kk);
+        }
+    }
+    const bool row_lane = book && tid < M, req_lane = book && tid >= 64 && tid - 64 < fin.B;
+    const int rr = row_lane ? tid / fin.W : (req_lane ? tid - 64 : 0);
+    const int ri = row_lane ? tid - rr * fin.W : 0;
+    int32_t c = 0, n_acc = 0, lim = 0;
+    uint8_t dmy = 0, rv = 1;
+    if (row_lane || req_lane) {
+        c = fin.nr.ctx_len_in[rr];
+        if (fin.store || fin.advance) {
+            n_acc = fin.n_acc[rr];
+            lim = fin.limit[rr];
+            dmy = fin.dummy[rr];
+        }
+        if (row_lane && fin.store && fin.row_valid) rv = fin.row_valid[tid];
+    }
+    for (int n = wave; n < M; n += WAVES) {  // rinv[n] = 1/sqrt(mean(f[n]^2) + eps), fixed order
+        float ss = 0.f;
+        for (int tt = lane; tt < p.T_in; tt += 64) ss += p.ss_in[(int64_t)tt * M + n];
+        ss = wave_sum(ss);
+        if (lane == 0) sh_rinv[n] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kStageChunks; ++i) {
+        const int idx = tid + i * NT;
+        if (idx < M * c8n) {
+            const int n = idx / c8n, c8 = idx - (idx / c8n) * c8n;
+            const float rinv = sh_rinv[n];
+            u32x4 gv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                gv[e] = pack2(bf_lo(wv[i][e]) * (bf_lo(fv[i][e]) * rinv), bf_hi(wv[i][e]) * (bf_hi(fv[i][e]) * rinv));
+            *(u32x4 *)(sh_g + n * ldg + (c8 << 3)) = gv;
+        }
+    }
+    // Group 0's second hop, issued now and stored only after the GEMM: the row's block-table entry
+    // (when it passes the write predicate), the request's bonus token, the rows' cos/sin values.
+    int64_t pos = 0, pidx = 0;
+    bool wr = false;
+    int32_t page = -1, bonus = 0;
+    if (row_lane && fin.store) {
+        wr = row_write_pred(fin, c, n_acc, lim, dmy, rv, ri, pos, pidx);
+        if (wr) page = fin.bt[(int64_t)rr * fin.bt_stride + pidx];
+    }
+    if (req_lane && fin.advance) {
+        const int nb = n_acc < 1 ? 1 : (n_acc > fin.W ? fin.W : n_acc);
+        bonus = fin.acc[(int64_t)rr * fin.acc_sr + (int64_t)(nb - 1) * fin.acc_st];
+    }
+    __syncthreads();
+    constexpr int CSN = kKvMaxRows * 256 / kKvThreads;  // cos/sin values per thread, at most
+    float csv[CSN];
+    const int rot = fin.nr.rope_dim;
+    if (book && fin.norm) {
+        // the rows' positions, for the cos/sin rows (ctx from row lanes, through LDS)
+        int *sh_pos = (int *)sh_rinv;   // sh_rinv is free again: g is staged
+        if (row_lane) {
+            const int64_t cp = (int64_t)c + ri;
+            sh_pos[tid] = (int)(cp < 0 ? 0 : (cp > fin.nr.cache_len - 1 ? fin.nr.cache_len - 1 : cp));
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < CSN; ++k) {
+            const int e = tid + k * NT;
+            csv[k] = e < M * rot ? fin.nr.cos_sin[(int64_t)sh_pos[e / rot] * rot + (e - (e / rot) * rot)] : 0.f;
+        }
+    }
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int f0 = 0; f0 < total; f0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int f = f0 + d;
+            if (f >= total) break;
+            const int i = f / nbw, j = f - (f / nbw) * nbw;
+            const int kl = (wave + j * WAVES) * 128;  // k offset inside the split
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const u32x4 v = c16 < M ? *(const u32x4 *)(sh_g + c16 * ldg + kl + (u * 4 + q) * 8)
+                                        : u32x4{0u, 0u, 0u, 0u};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a[d][u]),
+                                                              __builtin_bit_cast(bf16x8, v), acc, 0, 0, 0);
+            }
+            if (f + D < total) load(d, f + D);
+            if (j == nbw - 1) {
+                // tile i done: wave sums into red[i & 1], then the workgroup adds them in wave order
+                float *rb = red + (i & 1) * (WAVES * 16 * NP);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) rb[(wave * 16 + q * 4 + v) * NP + c16] = acc[v];
+                acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                __syncthreads();
+                const int t = t0 + i;
+                for (int idx = tid; idx < 16 * M; idx += NT) {
+                    const int o = idx & 15, n = idx >> 4;
+                    float y = 0.f;
+#pragma unroll
+                    for (int w = 0; w < WAVES; ++w) y += rb[(w * 16 + o) * NP + n];
+                    p.part[((int64_t)s * M + n) * p.O + t * 16 + o] = y;
+                }
+            }
+        }
+    }
+
+    if (!book) return;
+    // group 0: what the finalize needs of the rows and requests
+    void *bk = kp.book;
+    if (row_lane)
+        book_slot(bk)[tid] =
+            (wr && page >= 0 && page < fin.num_pages) ? (int64_t)page * fin.pg + (pos - pidx * fin.pg) : -1;
+    if (req_lane) {
+        const int64_t adv = (int64_t)c + n_acc;
+        book_ctx(bk)[rr] = c;
+        book_ctx_new(bk)[rr] = dmy ? 0 : (int32_t)(adv < (int64_t)lim ? adv : (int64_t)lim);
+        book_bonus(bk)[rr] = bonus;
+    }
+    if (fin.norm) {
+#pragma unroll
+        for (int k = 0; k < CSN; ++k) {
+            const int e = tid + k * NT;
+            if (e < M * rot) book_cs(bk)[e] = csv[k];
+        }
+    }
+}
+
+size_t kv_book_bytes(int rot) { return (size_t)kKvBookCs + (size_t)kKvMaxRows * (size_t)rot * 4; }
+
+static size_t up16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+hipError_t launch_kv(const KvParams &params, hipStream_t s) {
+    if (params.fin.M <= 0) return hipSuccess;
+    KvParams p = params;
+    const int tpu = p.unit_cols / 16;
+    if (p.kv.nbs % kKvWaves != 0 || p.kv.nbs <= 0 || p.ntg <= 0 || p.ntg > tpu || p.n_groups % p.kv.S != 0 ||
+        p.fin.M > kKvMaxRows || p.fin.B > kKvMaxRows || p.fin.nr.rope_dim > 256)
+        return hipErrorInvalidValue;
+    const size_t M = (size_t)p.kv.M;
+    const size_t g_bytes = M * (size_t)(p.kv.nbs * 128 + 8) * 2;
+    hipError_t e = launch1(k_kvgroups, dim3((unsigned)p.n_groups), dim3(kKvThreads), s, p, g_bytes);
+    if (e != hipSuccess) return e;
+    // finalize LDS: the rows [M][unit_cols] bf16, the k_norm weights, the rows' cos/sin values
+    p.lds_wk = (int32_t)up16(M * (size_t)p.unit_cols * 2);
+    p.lds_cs = (int32_t)(p.lds_wk + up16((size_t)p.unit_cols * 2));
+    const size_t fin_bytes = (size_t)p.lds_cs + M * (size_t)p.fin.nr.rope_dim * 4;
+    return launch1(k_kvfinal, dim3((unsigned)p.n_units), dim3(kKvThreads), s, p, fin_bytes);
+}
+
+}  // namespace dfkv
