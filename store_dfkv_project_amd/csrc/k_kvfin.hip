@@ -25,7 +25,7 @@
 // that no dependent load sits on the step's tail.
 //
 // k_kvfinal: one workgroup per unit -- a GQA K or V head, or an MLA layer's
-// latent + rope: one round of loads (the unit's split partials, its k_norm
+// latent + rope -- and block of rows: one round of loads (the unit's split partials, its k_norm
 // weights, the rows' cos/sin values and slots), then the per-head arithmetic of
 // finalize_common.hpp into kv_out and the pools; workgroup 0 also writes the
 // bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
@@ -59,15 +59,19 @@ __device__ __forceinline__ float *book_cs(void *b) { return (float *)((char *)b 
 // k_kvfinal: one workgroup per unit
 // ---------------------------------------------------------------------------
 
-// Unit u for every row: a GQA K or V head (columns [u*hd, (u+1)*hd)) or an MLA layer (latent +
-// rope).  Phase A (all threads, one round of loads): the unit's split partials summed in split order
-// and rounded to bf16, its k_norm weights, the rows' cos/sin values and slots, into LDS.  Phase B:
-// one wave per row, the per-head arithmetic of finalize_common.hpp, into kv_out and the pools.
+// Unit u (a GQA K or V head: columns [u*hd, (u+1)*hd); an MLA layer: latent + rope) for the rows
+// [n0, n0 + rpw) -- as many rows as keep the unit's partials one round of loads.  Phase A (all
+// threads, one round of loads): the split partials summed in split order and rounded to bf16, the
+// k_norm weights, the rows' cos/sin values and slots, into LDS.  Phase B: one wave per row, the
+// per-head arithmetic of finalize_common.hpp, into kv_out and the pools.
 __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     extern __shared__ __attribute__((aligned(16))) uint16_t sh_dyn[];
     const FinalizeParams &p = kp.fin;
-    const int u = blockIdx.x;
-    const int M = p.M, O = p.O, S = p.S;
+    const int nrb = (p.M + kp.fin_rows - 1) / kp.fin_rows;
+    const int u = blockIdx.x / nrb, rb = blockIdx.x - (blockIdx.x / nrb) * nrb;
+    const int n0 = rb * kp.fin_rows;
+    const int M = p.M - n0 < kp.fin_rows ? p.M - n0 : kp.fin_rows;  // rows of this workgroup
+    const int Mall = p.M, O = p.O, S = p.S;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int cols = kp.unit_cols;
     const bool gqa = p.kind == DFKV_GQA;
@@ -100,7 +104,8 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
                 const int n = e / cols, c = e - (e / cols) * cols;
 #pragma unroll
                 for (int k = 0; k < SB; ++k)
-                    v[i][k] = (e < total && s0 + k < S) ? p.part[((int64_t)(s0 + k) * M + n) * O + col0 + c] : 0.f;
+                    v[i][k] = (e < total && s0 + k < S) ? p.part[((int64_t)(s0 + k) * Mall + n0 + n) * O + col0 + c]
+                                                         : 0.f;
             }
 #pragma unroll
             for (int i = 0; i < EB; ++i)
@@ -117,10 +122,10 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     if (norm) {
         const uint16_t *w = p.nr.w_knorm + (int64_t)l * nwk;
         for (int c = tid; c < nwk; c += kKvThreads) wk[c] = w[c];
-        const float *bcs = book_cs(book);
+        const float *bcs = book_cs(book) + (int64_t)n0 * rot;
         for (int e = tid; e < M * rot; e += kKvThreads) cs[e] = bcs[e];
     }
-    if (tid < M) sh_slot[tid] = p.store ? book_slot(book)[tid] : -1;
+    if (tid < M) sh_slot[tid] = p.store ? book_slot(book)[n0 + tid] : -1;
     __syncthreads();
 
     // phase B
@@ -148,7 +153,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
                 }
             }
             const int64_t slot = sh_slot[n];
-            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)n * O + col0 : nullptr;
+            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)(n0 + n) * O + col0 : nullptr;
             uint16_t *d = slot >= 0 ? pool + slot_offset(p, slot) + (int64_t)h * p.sh : nullptr;
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
@@ -180,7 +185,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
                 rb = bf2f(y[n * cols + R + lane + half]);
             }
             const int64_t slot = sh_slot[n];
-            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)n * O + col0 : nullptr;
+            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)(n0 + n) * O + col0 : nullptr;
             uint16_t *d = slot >= 0 ? p.pk[l] + slot_offset(p, slot) : nullptr;
             const float rinv = norm ? latent_rinv(v, R, p.nr.eps) : 1.f;
 #pragma unroll
@@ -212,14 +217,15 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
 
     // workgroup 0: the bookkeeping outputs (slot, write mask, context positions; bonus, embedding
     // ids, query positions, advanced ctx_len, seq_len)
-    if (u != 0) return;
-    if (p.store && tid < M) {
-        p.slot[tid] = sh_slot[tid];
-        p.wmask[tid] = sh_slot[tid] >= 0 ? 1 : 0;
+    if (blockIdx.x != 0) return;
+    if (p.store && tid < Mall) {
+        const int64_t slot = book_slot(book)[tid];
+        p.slot[tid] = slot;
+        p.wmask[tid] = slot >= 0 ? 1 : 0;
     }
     if (!p.advance) return;
     const int32_t *ctx = book_ctx(book), *ctx_new = book_ctx_new(book), *bonus = book_bonus(book);
-    for (int e = tid; e < M; e += kKvThreads) {
+    for (int e = tid; e < Mall; e += kKvThreads) {
         const int r = e / p.W, i = e - (e / p.W) * p.W;
         p.c_pos[e] = (int32_t)((int64_t)ctx[r] + i);
     }
@@ -424,11 +430,17 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     const size_t g_bytes = M * (size_t)(p.kv.nbs * 128 + 8) * 2;
     hipError_t e = launch1(k_kvgroups, dim3((unsigned)p.n_groups), dim3(kKvThreads), s, p, g_bytes);
     if (e != hipSuccess) return e;
-    // finalize LDS: the rows [M][unit_cols] bf16, the k_norm weights, the rows' cos/sin values
-    p.lds_wk = (int32_t)up16(M * (size_t)p.unit_cols * 2);
+    // finalize: rows per workgroup such that the unit's partials are one round of loads (2 per
+    // thread) and each row has its own wave; LDS: the rows [rows][unit_cols] bf16, the k_norm
+    // weights, the rows' cos/sin values
+    int rows = 2 * kKvThreads / p.unit_cols;
+    rows = rows < 1 ? 1 : (rows > kKvWaves ? kKvWaves : rows);
+    p.fin_rows = rows;
+    p.lds_wk = (int32_t)up16((size_t)rows * (size_t)p.unit_cols * 2);
     p.lds_cs = (int32_t)(p.lds_wk + up16((size_t)p.unit_cols * 2));
-    const size_t fin_bytes = (size_t)p.lds_cs + M * (size_t)p.fin.nr.rope_dim * 4;
-    return launch1(k_kvfinal, dim3((unsigned)p.n_units), dim3(kKvThreads), s, p, fin_bytes);
+    const size_t fin_bytes = (size_t)p.lds_cs + (size_t)rows * (size_t)p.fin.nr.rope_dim * 4;
+    const unsigned nrb = (unsigned)((M + rows - 1) / rows);
+    return launch1(k_kvfinal, dim3((unsigned)p.n_units * nrb), dim3(kKvThreads), s, p, fin_bytes);
 }
 
 }  // namespace dfkv
