@@ -15,7 +15,7 @@ per-step graph launch, whose cost is reported separately
 (us_per_step_single_graph_replay).  A spin kernel is queued first so the host
 runs ahead of the GPU.
 
-Dominant kernel: the fc GEMM (k_stream at <= 64 rows, k_tiled above), timed
+Dominant kernel: the fc GEMM (k_stream at <= 64 rows, k_gemm above), timed
 as back-to-back dfkv_project_fc launches inside one graph; the K/V stage
 (dfkv_project_kv) is timed the same way and reported beside it.  At <= 16 rows
 the step is two kernels (fc, then K/V with the finalize, store and advance in
@@ -217,7 +217,7 @@ def main() -> int:
         achieved = alg["fc_flops"] / (fc_mean * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
-                    kernel="k_tiled (dfkv_project_fc: the fc GEMM) + k_hidden_norm",
+                    kernel="k_gemm (dfkv_project_fc: the fc GEMM) + k_hidden_norm",
                     algorithmic_flops_per_launch=alg["fc_flops"])
     roof.update(launch_us_mean=round(fc_mean, 2), launch_us_p10=round(float(np.percentile(fc_us, 10)), 2),
                 launch_us_p90=round(float(np.percentile(fc_us, 90)), 2))

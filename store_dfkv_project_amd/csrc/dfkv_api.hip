@@ -105,14 +105,27 @@ bool choose_kv_groups(const dfkv_geom *g, int64_t M, int *S_out, int *ntg_out) {
     return true;
 }
 
+// The large-batch fc GEMM is split over k when its output tiles leave most of the 256 CUs idle
+// (one workgroup per CU): enough splits to reach about one workgroup per CU, each split at least
+// 16 k steps of 64, at most 8 splits.
+int choose_fc_splits(int64_t M, int64_t H, int64_t K) {
+    const int tiles = gemm_tiles((int)M, (int)H);
+    if (tiles >= 192) return 1;
+    int S = 256 / tiles;
+    S = S < 8 ? S : 8;
+    while (S > 1 && K / 64 / S < 16) --S;
+    return S < 1 ? 1 : S;
+}
+
 struct Plan {
     int64_t M;
     bool skinny;
     bool kvfin;  // k_kvgroups + k_kvfinal run the K/V stage
     int S_kv;
+    int S_fc;    // large batch: k splits of the fc GEMM (partials summed by hidden_norm)
     int ntg;     // k_kvfin: tiles per K/V group
     // bookkeeping area of the small-batch K/V kernels; f [M][H]; small batch: ss [H/16][M] and K/V
-    // partials [S][M][O]; large batch: g [M][H]
+    // partials [S][M][O]; large batch: g [M][H] and, when the fc GEMM is split, its partials [S][M][H]
     size_t off_book, off_f, off_g, off_ss, off_part, total;
 };
 
@@ -140,7 +153,10 @@ dfkv_status make_plan(const dfkv_geom *g, int32_t n_reqs, Plan *pl) {
         p.off_part = off; off = up256(off + (size_t)p.S_kv * Mp * O * 4);
     } else {
         p.S_kv = 1;
-        p.off_ss = p.off_part = 0;
+        p.S_fc = choose_fc_splits(M, H, k_in(g));
+        p.off_ss = 0;
+        p.off_part = off;
+        if (p.S_fc > 1) off = up256(off + (size_t)p.S_fc * Mp * H * 4);
     }
     p.total = off;
     *pl = p;
@@ -391,14 +407,16 @@ dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int
         p.ss_out = (float *)(wsb + pl.off_ss);
         e = launch_stream(p, s);
     } else {
-        TiledParams t{(const uint16_t *)hidden, ld, (const uint16_t *)w_fc, f, H, (int32_t)pl.M, (int32_t)K,
-                      (int32_t)H};
-        e = launch_tiled(t, s);
+        float *part = pl.S_fc > 1 ? (float *)(wsb + pl.off_part) : nullptr;
+        GemmParams t{(const uint16_t *)hidden, ld, (const uint16_t *)w_fc, f, H, part, (int32_t)pl.M, (int32_t)K,
+                     (int32_t)H, (int32_t)pl.S_fc};
+        e = launch_gemm(t, s);
     }
     if (e != hipSuccess) return hip_status(e);
     if (stages_g(pl)) return DFKV_OK;
     uint16_t *gb = (uint16_t *)(wsb + pl.off_g);
-    return hip_status(launch_hidden_norm(f, (const uint16_t *)w_hnorm, gb, (int)pl.M, (int)H, g->eps, s));
+    const float *part = !pl.skinny && pl.S_fc > 1 ? (const float *)(wsb + pl.off_part) : nullptr;
+    return hip_status(launch_hidden_norm(f, part, pl.S_fc, (const uint16_t *)w_hnorm, gb, (int)pl.M, (int)H, g->eps, s));
 }
 
 dfkv_status run_kvfin(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx, const float *cs,
@@ -443,8 +461,9 @@ dfkv_status run_kv(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx
         return hip_status(launch_finalize(fin, s));
     }
     const uint16_t *gb = (const uint16_t *)(wsb + pl.off_g);
-    TiledParams t2{gb, H, (const uint16_t *)w->w_kv, (uint16_t *)kv_out, O, (int32_t)pl.M, (int32_t)H, (int32_t)O};
-    if ((e = launch_tiled(t2, s)) != hipSuccess) return hip_status(e);
+    GemmParams t2{gb, H, (const uint16_t *)w->w_kv, (uint16_t *)kv_out, O, nullptr, (int32_t)pl.M, (int32_t)H,
+                  (int32_t)O, 1};
+    if ((e = launch_gemm(t2, s)) != hipSuccess) return hip_status(e);
     if (!fuse && !need_finalize) return DFKV_OK;
     fin.part = nullptr;
     fin.src = (const uint16_t *)kv_out;  // in place: each element is read and written by one thread

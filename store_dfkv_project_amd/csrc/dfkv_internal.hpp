@@ -107,8 +107,9 @@ struct FinalizeParams {
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s);
 hipError_t launch_advance(const FinalizeParams &p, hipStream_t s);
 
-hipError_t launch_hidden_norm(const uint16_t *f, const uint16_t *w, uint16_t *g, int n_rows, int H, float eps,
-                              hipStream_t s);
+// part != null: f = bf16(sum of the S fp32 partials [S][n_rows][H]) is formed and written first
+hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint16_t *w, uint16_t *g, int n_rows,
+                              int H, float eps, hipStream_t s);
 hipError_t launch_rope_cache(const dfkv_rope &r, float *cs, int cache_len, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
@@ -153,15 +154,18 @@ struct KvParams {
 hipError_t launch_kv(const KvParams &p, hipStream_t s);
 size_t kv_book_bytes(int rot);
 
-// Tiled MFMA GEMM for larger M: out[n][o] = bf16(sum_k x[n][k] w[o][k]).
-struct TiledParams {
+// 256 x 256-tile MFMA GEMM with an LDS ring fed by direct-to-LDS loads (k_gemm.hip):
+// out = bf16(x . w^T), or with S > 1 splits of k, fp32 partial sums part[S][M][O].
+struct GemmParams {
     const uint16_t *x;
     int64_t ldx;
     const uint16_t *w;
     uint16_t *out;
     int64_t ldo;
-    int32_t M, K, O;
+    float *part;
+    int32_t M, K, O, S;
 };
-hipError_t launch_tiled(const TiledParams &p, hipStream_t s);
+hipError_t launch_gemm(const GemmParams &p, hipStream_t s);
+int gemm_tiles(int M, int O);   // output tiles of launch_gemm (times S workgroups)
 
 }  // namespace dfkv

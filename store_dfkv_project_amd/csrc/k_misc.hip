@@ -9,26 +9,47 @@ namespace dfkv {
 // ---------------------------------------------------------------------------
 // hidden_norm: g[n][:] = bf16(w * f[n][:] / sqrt(mean(f[n]^2) + eps)); one
 // workgroup per row (used by the large-batch path; the small-batch path folds
-// it into the stacked GEMM's operand load).
+// it into the stacked GEMM's operand load).  When the fc GEMM was split over
+// k, f is first formed here: f = bf16(sum over the S fp32 partials, in split
+// order), written out and then normalised.
 // ---------------------------------------------------------------------------
 struct HiddenNormArgs {
-    const uint16_t *f, *w;
-    uint16_t *g;
-    int H;
+    const uint16_t *w;
+    uint16_t *f, *g;
+    const float *part;   // [S][n_rows][H] fp32 partial sums of f, or null (f is given)
+    int S, n_rows, H;
     float eps;
 };
 
 __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
-    const uint16_t *f = a.f, *w = a.w;
+    const uint16_t *w = a.w;
     uint16_t *g = a.g;
     const int H = a.H;
     const float eps = a.eps;
     const int row = blockIdx.x;
-    const uint16_t *x = f + (int64_t)row * H;
+    uint16_t *x = a.f + (int64_t)row * H;
     __shared__ float red[4];
     float ss = 0.f;
     for (int c = threadIdx.x; c < (H >> 3); c += blockDim.x) {
-        const u32x4 v = *(const u32x4 *)(x + (c << 3));
+        u32x4 v;
+        if (a.part) {
+            // each thread writes and later re-reads the same chunks of f: no cross-thread hand-off
+            float s8[8];
+            const float *src = a.part + (int64_t)row * H + (c << 3);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s8[e] = 0.f;
+            for (int sp = 0; sp < a.S; ++sp) {
+                const float4 lo = *(const float4 *)(src + (int64_t)sp * a.n_rows * H);
+                const float4 hi = *(const float4 *)(src + (int64_t)sp * a.n_rows * H + 4);
+                s8[0] += lo.x; s8[1] += lo.y; s8[2] += lo.z; s8[3] += lo.w;
+                s8[4] += hi.x; s8[5] += hi.y; s8[6] += hi.z; s8[7] += hi.w;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = pack2(s8[2 * q], s8[2 * q + 1]);
+            *(u32x4 *)(x + (c << 3)) = v;
+        } else {
+            v = *(const u32x4 *)(x + (c << 3));
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             float a = bf_lo(v[q]), b = bf_hi(v[q]);
@@ -51,10 +72,11 @@ __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
     }
 }
 
-hipError_t launch_hidden_norm(const uint16_t *f, const uint16_t *w, uint16_t *g, int n_rows, int H, float eps,
-                              hipStream_t s) {
+hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint16_t *w, uint16_t *g, int n_rows,
+                              int H, float eps, hipStream_t s) {
     if (n_rows == 0) return hipSuccess;
-    return launch1(k_hidden_norm, dim3(n_rows), dim3(256), s, HiddenNormArgs{f, w, g, H, eps});
+    if (H % 8 != 0 || (part && S < 1)) return hipErrorInvalidValue;
+    return launch1(k_hidden_norm, dim3(n_rows), dim3(256), s, HiddenNormArgs{w, f, g, part, S, n_rows, H, eps});
 }
 
 // ---------------------------------------------------------------------------
