@@ -74,9 +74,10 @@ class Oracle:
         L.dfkv_oracle_bookkeeping.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _I64, _I, _I,
                                               _P, _I64, _I64, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P]
         L.dfkv_oracle_store.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64, _I64, _I64]
+        L.dfkv_oracle_block_placement.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I64, _I, _I, _P]
         for fn in ("dfkv_oracle_linear", "dfkv_oracle_rmsnorm", "dfkv_oracle_inv_freq", "dfkv_oracle_rope_cache",
                    "dfkv_oracle_rope_neox", "dfkv_oracle_norm_rope", "dfkv_oracle_project",
-                   "dfkv_oracle_bookkeeping", "dfkv_oracle_store"):
+                   "dfkv_oracle_bookkeeping", "dfkv_oracle_store", "dfkv_oracle_block_placement"):
             getattr(L, fn).restype = None
         self.lib = L
 
@@ -201,7 +202,23 @@ class Oracle:
         out["emb_ids"] = out["emb_ids"].reshape(B, bs)
         out["q_pos"] = out["q_pos"].reshape(B, bs)
         out["c_pos"] = out["c_pos"].reshape(B, W)
+        out["block_slot"] = self.block_placement(geom, n_reqs, out["ctx_len"], alloc_limit, is_dummy, bt, bt_stride,
+                                                 bt_cols, num_pages)
         return out
+
+    def block_placement(self, geom, n_reqs, ctx_new, alloc_limit, is_dummy, block_table, bt_stride, bt_cols,
+                        num_pages) -> np.ndarray:
+        """Slots of the next draft block's own positions ctx' + j, j < block_size ([B, block_size] int64, -1 where
+        the position is not in an allocated page): the block placement of the downstream commit quoted on the
+        PR #20550 page."""
+        B, bs = n_reqs, geom.block_size
+        out = np.empty(B * bs, np.int64)
+        ins = [np.ascontiguousarray(a, dtype=t) for a, t in ((ctx_new, np.int32), (alloc_limit, np.int32),
+                                                             (is_dummy, np.uint8))]
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        self.lib.dfkv_oracle_block_placement(B, bs, geom.page_size, *[_ptr(a) for a in ins], _ptr(bt), bt_stride,
+                                             bt_cols, num_pages, _ptr(out))
+        return out.reshape(B, bs)
 
     def store(self, geom, kv: np.ndarray, slot: np.ndarray, write_mask: np.ndarray, pools_k: Sequence[np.ndarray],
               pools_v: Optional[Sequence[np.ndarray]], s_page: int, s_slot: int, s_head: int) -> None:

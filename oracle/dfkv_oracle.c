@@ -397,6 +397,42 @@ EXPORT void dfkv_oracle_bookkeeping(int B, int W, int bs_blk, int pg,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Block placement (the downstream commit quoted on the PR #20550 page: the  */
+/* bookkeeping kernel also places the next draft block's own positions in    */
+/* the pages, which the drafter's block decode takes instead of gathering    */
+/* the page table again).  For request r and j < bs_blk, with ctx' from the  */
+/* advance above:                                                            */
+/*   pos = ctx' + j                               (the block's query position) */
+/*   v   = !d && 0 <= pos < lim && pos/pg < bt_cols && 0 <= page < num_pages */
+/*         with page = block_table[r][pos/pg]                                */
+/*   block_slot[r][j] = v ? page*pg + pos%pg : -1                            */
+/* ------------------------------------------------------------------------ */
+
+EXPORT void dfkv_oracle_block_placement(int B, int bs_blk, int pg, const int32_t *ctx_new,
+                                        const int32_t *alloc_limit, const uint8_t *is_dummy,
+                                        const int32_t *bt, int64_t bt_stride, int bt_cols, int num_pages,
+                                        int64_t *block_slot_out)
+{
+    for (int r = 0; r < B; ++r) {
+        const int32_t *bt_row = bt + (int64_t)r * bt_stride;
+        for (int j = 0; j < bs_blk; ++j) {
+            int64_t pos = (int64_t)ctx_new[r] + j;
+            int64_t slot = -1;
+#if DFKV_ORACLE_MUTANT == 8 /* planted: the block may reach one position past the allocation */
+            if (!is_dummy[r] && pos >= 0 && pos <= alloc_limit[r] && pos / pg < bt_cols) {
+#else
+            if (!is_dummy[r] && pos >= 0 && pos < alloc_limit[r] && pos / pg < bt_cols) {
+#endif
+                int32_t page = bt_row[pos / pg];
+                if (page >= 0 && page < num_pages)
+                    slot = (int64_t)page * pg + pos % pg;
+            }
+            block_slot_out[(int64_t)r * bs_blk + j] = slot;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Paged store: every written row goes into every layer's pool.              */
 /* GQA: layer l's K pool gets kv[row][l][0][h][:] at                         */
 /*      page*s_page + off*s_slot + h*s_head, its V pool kv[row][l][1][h][:]. */

@@ -478,6 +478,94 @@ def pin_golden_bookkeeping(o):
 
 
 # ---------------------------------------------------------------------------
+# block placement: the next draft block's own positions in the pages
+# ---------------------------------------------------------------------------
+
+def _expected_placement_position_first(bs, pg, ctx_new, lim, dummy, bt, num_pages):
+    """Walk every table entry (column q, offset off) of each request and place the position it holds
+    into the block when that position is one of ctx' .. ctx'+bs-1 inside the allocation."""
+    B, cols = bt.shape
+    want = np.full((B, bs), -1, np.int64)
+    for r in range(B):
+        if dummy[r]:
+            continue
+        for q in range(cols):
+            page = int(bt[r, q])
+            if not 0 <= page < num_pages:
+                continue
+            for off in range(pg):
+                p = q * pg + off
+                j = p - int(ctx_new[r])
+                if 0 <= j < bs and p < lim[r]:
+                    want[r, j] = page * pg + off
+    return want
+
+
+def pin_block_placement_bruteforce(o):
+    geom_base = dict(kind=GQA, n_tgt=1, tgt_hidden=8, hidden=8, n_layers=1, n_kv_heads=1, head_dim=8,
+                     latent_dim=0, rope_dim=8, eps=1e-6)
+    rng = np.random.default_rng(63)
+    checked = 0
+    for W, pg, cols, bs in ((1, 1, 4, 1), (2, 2, 3, 3), (3, 4, 2, 5), (4, 2, 4, 2), (4, 4, 3, 7)):
+        geom = Geometry(page_size=pg, width=W, block_size=bs, **geom_base)
+        num_pages = 16
+        for c, n, lim in itertools.product(range(0, 21, 3), range(0, W + 1), range(0, 17, 2)):
+            for dummy in (0, 1):
+                tbl = rng.permutation(num_pages)[:2 * cols].reshape(2, cols).astype(np.int32)
+                neg = rng.random((2, cols)) < 0.25
+                tbl[neg] = -1 - rng.integers(0, 3, size=int(neg.sum()))
+                if rng.random() < 0.1:
+                    tbl[0, :] = 99
+                ctx = np.array([c, rng.integers(0, 12)], np.int32)
+                na = np.array([n, rng.integers(0, W + 1)], np.int32)
+                lm = np.array([lim, rng.integers(0, 16)], np.int32)
+                dm = np.array([dummy, 0], np.uint8)
+                acc = rng.integers(0, 1000, size=(2, W)).astype(np.int32)
+                out = o.bookkeeping(geom, 2, ctx, na, lm, dm, None, tbl, acc, W, 1, 777, num_pages)
+                want = _expected_placement_position_first(bs, pg, out["ctx_len"], lm, dm, tbl, num_pages)
+                assert np.array_equal(out["block_slot"], want), (W, pg, c, n, lim, dummy, out["block_slot"], want)
+                checked += 1
+    assert checked > 1000
+
+
+def pin_block_placement_matches_row_slots(o):
+    """With nothing accepted the block starts at the pre-step context length, so its j-th position is the
+    position of verify row j: when every row is accepted instead, row j's slot must equal the block's j-th
+    placement (the row-slot formula is pinned by brute force above)."""
+    geom = Geometry(kind=GQA, n_tgt=1, tgt_hidden=8, hidden=8, n_layers=1, n_kv_heads=1, head_dim=8, latent_dim=0,
+                    rope_dim=8, eps=1e-6, page_size=4, width=4, block_size=6)
+    rng = np.random.default_rng(64)
+    B, cols, P = 8, 6, 64
+    for _ in range(40):
+        tbl = rng.permutation(P)[:B * cols].reshape(B, cols).astype(np.int32)
+        tbl[rng.random((B, cols)) < 0.2] = -1
+        ctx = rng.integers(0, 20, size=B).astype(np.int32)
+        lim = (ctx + rng.integers(0, 8, size=B)).astype(np.int32)
+        dm = (rng.random(B) < 0.2).astype(np.uint8)
+        acc = rng.integers(0, 1000, size=(B, 4)).astype(np.int32)
+        none = o.bookkeeping(geom, B, ctx, np.zeros(B, np.int32), lim, dm, None, tbl, acc, 4, 1, 5, P)
+        full = o.bookkeeping(geom, B, ctx, np.full(B, 4, np.int32), lim, dm, None, tbl, acc, 4, 1, 5, P)
+        for r in range(B):
+            for j in range(4):
+                assert none["block_slot"][r, j] == full["slot"][r * 4 + j], (r, j)
+
+
+def pin_golden_block_placement(o):
+    """A case worked by hand (tests/golden/block_placement_tiny.json)."""
+    with open(os.path.join(GOLDEN, "block_placement_tiny.json")) as fh:
+        g = json.load(fh)
+    geom = Geometry(kind=GQA, n_tgt=1, tgt_hidden=8, hidden=8, n_layers=1, n_kv_heads=1, head_dim=8, latent_dim=0,
+                    rope_dim=8, eps=1e-6, page_size=g["page_size"], width=g["width"], block_size=g["block_size"])
+    i = g["inputs"]
+    rv = None if i["row_valid"] is None else np.array(i["row_valid"], np.uint8)
+    out = o.bookkeeping(geom, len(i["ctx_len"]), np.array(i["ctx_len"], np.int32), np.array(i["n_acc"], np.int32),
+                        np.array(i["alloc_limit"], np.int32), np.array(i["is_dummy"], np.uint8), rv,
+                        np.array(i["block_table"], np.int32), np.array(i["accepted_tokens"], np.int32),
+                        g["width"], 1, i["mask_token_id"], i["num_pages"])
+    assert np.array_equal(out["block_slot"], np.array(g["expected"]["block_slot"], np.int64)), out["block_slot"]
+
+
+# ---------------------------------------------------------------------------
 # paged store
 # ---------------------------------------------------------------------------
 
