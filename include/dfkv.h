@@ -167,7 +167,17 @@ typedef struct dfkv_pool {
  *  q_pos       [B*block_size] int32  ctx_len_out + j
  *  ctx_len_out [B]   int32  dummy ? 0 : min(ctx_len_in + n_acc, alloc_limit)
  *                           (also the advertised context length)
- *  seq_len     [B]   int32  ctx_len_out + block_size */
+ *  seq_len     [B]   int32  ctx_len_out + block_size
+ *  block_slot  [B*block_size] int64 or NULL: placement of the next draft block's
+ *                           own positions q_pos in the pages ([P20550] downstream
+ *                           commit: the bookkeeping kernel places the block, which
+ *                           the drafter's block decode takes instead of gathering
+ *                           the page table again): page*page_size + offset of
+ *                           position q = q_pos[r][j], -1 when the request is a
+ *                           dummy, q >= alloc_limit, q/page_size >= bt_cols or the
+ *                           page is outside [0, num_pages).  Written by
+ *                           dfkv_store_advance and dfkv_step (which know the pool's
+ *                           page count); dfkv_advance requires it NULL. */
 typedef struct dfkv_outputs {
     int64_t *slot;
     uint8_t *write_mask;
@@ -177,6 +187,7 @@ typedef struct dfkv_outputs {
     int32_t *q_pos;
     int32_t *ctx_len_out;
     int32_t *seq_len;
+    int64_t *block_slot;
 } dfkv_outputs;
 
 /* RoPE parameters.  yarn = 0: plain RoPE (RoFormer), inverse frequencies
@@ -306,14 +317,16 @@ dfkv_status dfkv_paged_store(const dfkv_geom *g, const void *kv, const dfkv_requ
  * dummy-slot reset, advertised context length; downstream commit: seq_lens;
  * [P13995] "fuse query-input build": positions by broadcast-add, embedding ids
  * [bonus, mask...]).  Writes out->c_pos, bonus, emb_ids, q_pos, ctx_len_out,
- * seq_len (slot and write_mask are ignored and may be NULL).
+ * seq_len (slot and write_mask are ignored and may be NULL; block_slot must be
+ * NULL: placing the block needs the pool's page count, see dfkv_store_advance).
  * ctx_len_out must not overlap ctx_len_in (no in-place advance).
- * Errors: NULL, SHAPE, ALIAS, HIP. */
+ * Errors: NULL, SHAPE (also a non-NULL block_slot), ALIAS, HIP. */
 dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfkv_outputs *out,
                          dfkv_stream_t stream);
 
 /* dfkv_paged_store and dfkv_advance in one coalesced launch; writes every
- * field of *out.  Errors as the two calls. */
+ * field of *out (block_slot when it is not NULL: the block placement).
+ * Errors as the two calls. */
 dfkv_status dfkv_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
                                const dfkv_pool *pool, const dfkv_outputs *out, dfkv_stream_t stream);
 

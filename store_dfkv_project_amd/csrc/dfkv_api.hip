@@ -146,7 +146,8 @@ dfkv_status make_plan(const dfkv_geom *g, int32_t n_reqs, Plan *pl) {
     p.off_book = off; off = up256(off + kv_book_bytes(g->rope_dim));
     p.off_f = off; off = up256(off + Mp * H * 2);
     p.off_g = off; off = up256(off + Mp * H * 2);
-    p.kvfin = M >= 1 && M <= kKvMaxRows && choose_kv_groups(g, M, &p.S_kv, &p.ntg);
+    p.kvfin = M >= 1 && M <= kKvMaxRows && (int64_t)n_reqs * g->block_size <= kKvMaxBlockPositions &&
+              choose_kv_groups(g, M, &p.S_kv, &p.ntg);
     if (p.skinny) {
         if (!p.kvfin) p.S_kv = choose_kv_splits((int)(O / 16), (int)(H / 128), M);
         p.off_ss = off;   off = up256(off + (size_t)(H / 16) * Mp * 4);
@@ -316,6 +317,19 @@ dfkv_status check_adv_outputs(const dfkv_geom *g, const dfkv_requests *r, const 
                                       extent2(r->bt_row_stride, B, 1, r->bt_cols)))
             return DFKV_ERR_ALIAS;
     }
+    if (o->block_slot) {
+        // the block placement reads the block table: it needs one, and overlaps nothing
+        if (!r->block_table) return DFKV_ERR_NULL;
+        if (((uintptr_t)o->block_slot & 7) != 0) return DFKV_ERR_LAYOUT;
+        const size_t bb = (size_t)(B * bs) * 8;
+        for (int j = 0; j < 6; ++j)
+            if (overlap(o->block_slot, bb, ins[j], ib[j]) || overlap(o->block_slot, bb, outs[j], ob[j]))
+                return DFKV_ERR_ALIAS;
+        if (overlap(o->block_slot, bb, r->block_table, extent2(r->bt_row_stride, B, 1, r->bt_cols)))
+            return DFKV_ERR_ALIAS;
+        if (o->slot && overlap(o->block_slot, bb, o->slot, (size_t)N * 8)) return DFKV_ERR_ALIAS;
+        if (o->write_mask && overlap(o->block_slot, bb, o->write_mask, (size_t)N)) return DFKV_ERR_ALIAS;
+    }
     return DFKV_OK;
 }
 
@@ -367,6 +381,7 @@ FinalizeParams fin_params(const dfkv_geom *g, const dfkv_requests *r, const dfkv
         p.q_pos = o->q_pos;
         p.ctx_out = o->ctx_len_out;
         p.seq_len = o->seq_len;
+        p.block_slot = o->block_slot;
     }
     return p;
 }
@@ -672,6 +687,7 @@ dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfk
     dfkv_status st = check_geom(g);
     if (st != DFKV_OK) return st;
     if ((st = check_requests(g, req, false, true)) != DFKV_OK) return st;
+    if (out && out->block_slot) return DFKV_ERR_SHAPE;   // the placement needs the pool's page count
     if (req->n_reqs == 0) return DFKV_OK;
     if ((st = check_adv_outputs(g, req, out)) != DFKV_OK) return st;
     const FinalizeParams p = fin_params(g, req, nullptr, out, 0);

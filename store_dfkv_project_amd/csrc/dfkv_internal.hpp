@@ -103,6 +103,7 @@ struct FinalizeParams {
     int64_t *slot;
     uint8_t *wmask;
     int32_t *c_pos, *bonus, *emb, *q_pos, *ctx_out, *seq_len;
+    int64_t *block_slot;   // [B][bs_blk] or null: placement of the next draft block
 };
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s);
 hipError_t launch_advance(const FinalizeParams &p, hipStream_t s);
@@ -136,6 +137,8 @@ hipError_t launch_stream(const StreamParams &p, hipStream_t s);
 // K/V stage of the small-batch step (M <= 16 rows): hidden_norm + the stacked K/V GEMM as split-K
 // groups (k_kvgroups), then the finalize (k_kvfinal) -- k_kvfin.hip.
 constexpr int kKvMaxRows = 16;
+constexpr int kKvBlockLane0 = 128;  // k_kvgroups group 0: first lane placing the next draft block
+constexpr int kKvMaxBlockPositions = 512 - kKvBlockLane0;  // requests x block_size it can place
 constexpr int kKvSlots = 512;    // resident workgroups of k_kvgroups: 2 per CU x 256 CUs
 // Row/request bookkeeping left in the workspace by k_kvgroups for k_kvfinal (byte offsets):
 // slot int64 [16], ctx / ctx_new / bonus int32 [16] each, then the rows' cos/sin values fp32 [16][rot].

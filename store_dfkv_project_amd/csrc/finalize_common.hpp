@@ -55,6 +55,28 @@ __device__ __forceinline__ int64_t slot_offset(const FinalizeParams &p, int64_t 
     return page * p.sp + (slot - page * p.pg) * p.ss;
 }
 
+// Placement of position ctx_new + j of the next draft block of request r (the downstream commit
+// quoted on the PR #20550 page: the bookkeeping places the block's own positions in the pages):
+// page * pg + offset, or -1 for a dummy request, a position outside [0, lim), past the block
+// table, or in a page outside [0, num_pages).
+__device__ __forceinline__ bool block_position_ok(const FinalizeParams &p, int32_t ctx_new, int32_t lim, bool d,
+                                                  int j, int64_t &pos, int64_t &pidx) {
+    pos = (int64_t)ctx_new + j;
+    pidx = 0;
+    if (d || pos < 0 || pos >= (int64_t)lim) return false;
+    pidx = pos / p.pg;
+    return pidx < p.bt_cols;
+}
+__device__ __forceinline__ int64_t block_page_slot(const FinalizeParams &p, int32_t page, int64_t pos, int64_t pidx) {
+    return (page >= 0 && page < p.num_pages) ? (int64_t)page * p.pg + (pos - pidx * p.pg) : -1;
+}
+__device__ __forceinline__ int64_t block_position_slot(const FinalizeParams &p, int r, int32_t ctx_new, int32_t lim,
+                                                       bool d, int j) {
+    int64_t pos, pidx;
+    if (!block_position_ok(p, ctx_new, lim, d, j, pos, pidx)) return -1;
+    return block_page_slot(p, p.bt[(int64_t)r * p.bt_stride + pidx], pos, pidx);
+}
+
 // The per-request outputs of request r, written by the calling workgroup.
 __device__ __forceinline__ void request_advance(const FinalizeParams &p, int r) {
     const int32_t c = p.ctx_len[r], n = p.n_acc[r], lim = p.limit[r];
@@ -68,6 +90,9 @@ __device__ __forceinline__ void request_advance(const FinalizeParams &p, int r) 
         p.q_pos[(int64_t)r * p.bs_blk + j] = ctx_new + j;
     }
     for (int j = threadIdx.x; j < p.W; j += blockDim.x) p.c_pos[(int64_t)r * p.W + j] = (int32_t)((int64_t)c + j);
+    if (p.block_slot)
+        for (int j = threadIdx.x; j < p.bs_blk; j += blockDim.x)
+            p.block_slot[(int64_t)r * p.bs_blk + j] = block_position_slot(p, r, ctx_new, lim, d, j);
     if (threadIdx.x == 0) {
         p.bonus[r] = bonus;
         p.ctx_out[r] = ctx_new;

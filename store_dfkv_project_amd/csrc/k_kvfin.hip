@@ -293,12 +293,17 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
             wv[i] = *(const u32x4 *)(p.w_hn + kk);
         }
     }
+    // (block lanes, from 128: one per position of the next draft block of each request)
     const bool row_lane = book && tid < M, req_lane = book && tid >= 64 && tid - 64 < fin.B;
-    const int rr = row_lane ? tid / fin.W : (req_lane ? tid - 64 : 0);
+    const bool blk_lane = book && fin.advance && fin.block_slot && tid >= kKvBlockLane0 &&
+                          tid - kKvBlockLane0 < fin.B * fin.bs_blk;
+    const int rr = row_lane ? tid / fin.W
+                            : (req_lane ? tid - 64 : (blk_lane ? (tid - kKvBlockLane0) / fin.bs_blk : 0));
     const int ri = row_lane ? tid - rr * fin.W : 0;
+    const int bj = blk_lane ? tid - kKvBlockLane0 - rr * fin.bs_blk : 0;
     int32_t c = 0, n_acc = 0, lim = 0;
     uint8_t dmy = 0, rv = 1;
-    if (row_lane || req_lane) {
+    if (row_lane || req_lane || blk_lane) {
         c = fin.nr.ctx_len_in[rr];
         if (fin.store || fin.advance) {
             n_acc = fin.n_acc[rr];
@@ -339,6 +344,15 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     if (req_lane && fin.advance) {
         const int nb = n_acc < 1 ? 1 : (n_acc > fin.W ? fin.W : n_acc);
         bonus = fin.acc[(int64_t)rr * fin.acc_sr + (int64_t)(nb - 1) * fin.acc_st];
+    }
+    int64_t bpos = 0, bpidx = 0;
+    int32_t bpage = -1;
+    bool bok = false;
+    if (blk_lane) {
+        const int64_t adv = (int64_t)c + n_acc;
+        const int32_t cn = dmy ? 0 : (int32_t)(adv < (int64_t)lim ? adv : (int64_t)lim);
+        bok = block_position_ok(fin, cn, lim, dmy != 0, bj, bpos, bpidx);
+        if (bok) bpage = fin.bt[(int64_t)rr * fin.bt_stride + bpidx];
     }
     __syncthreads();
     constexpr int CSN = kKvMaxRows * 256 / kKvThreads;  // cos/sin values per thread, at most
@@ -400,6 +414,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     if (row_lane)
         book_slot(bk)[tid] =
             (wr && page >= 0 && page < fin.num_pages) ? (int64_t)page * fin.pg + (pos - pidx * fin.pg) : -1;
+    if (blk_lane) fin.block_slot[tid - kKvBlockLane0] = bok ? block_page_slot(fin, bpage, bpos, bpidx) : -1;
     if (req_lane) {
         const int64_t adv = (int64_t)c + n_acc;
         book_ctx(bk)[rr] = c;

@@ -65,7 +65,7 @@ class dfkv_pool(C.Structure):
 class dfkv_outputs(C.Structure):
     _fields_ = [("slot", C.c_void_p), ("write_mask", C.c_void_p), ("c_pos", C.c_void_p), ("bonus", C.c_void_p),
                 ("emb_ids", C.c_void_p), ("q_pos", C.c_void_p), ("ctx_len_out", C.c_void_p),
-                ("seq_len", C.c_void_p)]
+                ("seq_len", C.c_void_p), ("block_slot", C.c_void_p)]
 
 
 class dfkv_rope(C.Structure):
@@ -195,9 +195,9 @@ def make_pool(k: Sequence, v: Optional[Sequence], stride_page: int, stride_slot:
 
 
 def make_outputs(slot=None, write_mask=None, c_pos=None, bonus=None, emb_ids=None, q_pos=None, ctx_len_out=None,
-                 seq_len=None) -> dfkv_outputs:
+                 seq_len=None, block_slot=None) -> dfkv_outputs:
     return dfkv_outputs(_ptr(slot), _ptr(write_mask), _ptr(c_pos), _ptr(bonus), _ptr(emb_ids), _ptr(q_pos),
-                        _ptr(ctx_len_out), _ptr(seq_len))
+                        _ptr(ctx_len_out), _ptr(seq_len), _ptr(block_slot))
 
 
 def make_rope(theta, rot, yarn=False, factor=1.0, orig_ctx=0.0, beta_fast=32.0, beta_slow=1.0,

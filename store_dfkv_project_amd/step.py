@@ -118,8 +118,13 @@ class DeviceStep:
         self.q_pos = torch.zeros(B * g.block_size, dtype=torch.int32, device=device)
         self.ctx_len_out = torch.zeros(B, dtype=torch.int32, device=device)
         self.seq_len = torch.zeros(B, dtype=torch.int32, device=device)
+        # block placement (written by store_advance / step; -7 marks an entry nothing wrote)
+        self.block_slot = torch.full((B * g.block_size,), -7, dtype=torch.int64, device=device)
         self.outs = dfkv.make_outputs(self.slot, self.write_mask, self.c_pos, self.bonus, self.emb_ids, self.q_pos,
-                                      self.ctx_len_out, self.seq_len)
+                                      self.ctx_len_out, self.seq_len, self.block_slot)
+        # dfkv_advance takes no pool, so it places no block
+        self.outs_adv = dfkv.make_outputs(self.slot, self.write_mask, self.c_pos, self.bonus, self.emb_ids,
+                                          self.q_pos, self.ctx_len_out, self.seq_len)
         # workspace
         self.ws_bytes = dfkv.dfkv_workspace_size(self.gs, B)
         self.ws = torch.empty(max(self.ws_bytes, 256), dtype=torch.uint8, device=device)
@@ -149,7 +154,7 @@ class DeviceStep:
                               self.write_mask, stream)
 
     def advance(self, stream=None):
-        dfkv.dfkv_advance(self.gs, self.req, self.outs, stream)
+        dfkv.dfkv_advance(self.gs, self.req, self.outs_adv, stream)
 
     def store_advance(self, kv=None, stream=None):
         dfkv.dfkv_store_advance(self.gs, self.kv_out if kv is None else kv, self.req, self.pool, self.outs, stream)
@@ -169,7 +174,8 @@ class DeviceStep:
                     c_pos=self.c_pos.cpu().numpy().reshape(B, g.width), bonus=self.bonus.cpu().numpy(),
                     emb_ids=self.emb_ids.cpu().numpy().reshape(B, g.block_size),
                     q_pos=self.q_pos.cpu().numpy().reshape(B, g.block_size),
-                    ctx_len=self.ctx_len_out.cpu().numpy(), seq_len=self.seq_len.cpu().numpy())
+                    ctx_len=self.ctx_len_out.cpu().numpy(), seq_len=self.seq_len.cpu().numpy(),
+                    block_slot=self.block_slot.cpu().numpy().reshape(B, g.block_size))
 
     def pool_slot_view(self, layer: int, half: int = 0) -> torch.Tensor:
         """Pool of one layer as [num_pages*page_size, slot_elems] rows (NHD / MLA layouts)."""

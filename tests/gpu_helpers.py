@@ -96,7 +96,7 @@ def oracle_bookkeeping(orc, wl: Workload) -> dict:
 
 
 def compare_bookkeeping(got: dict, want: dict, what: str = "") -> None:
-    for k in ("slot", "write_mask", "c_pos", "bonus", "emb_ids", "q_pos", "ctx_len", "seq_len"):
+    for k in ("slot", "write_mask", "c_pos", "bonus", "emb_ids", "q_pos", "ctx_len", "seq_len", "block_slot"):
         g, w = np.asarray(got[k]).reshape(-1), np.asarray(want[k]).reshape(-1)
         if not np.array_equal(g, w):
             i = int(np.nonzero(g != w)[0][0])

@@ -207,6 +207,20 @@ def test_advance_validation():
         dfkv.DFKV_ERR_LAYOUT
     assert status_of(dfkv.dfkv_advance, geom(), requests(n_acc=None), outputs(), stream=0) == dfkv.DFKV_ERR_NULL
     assert status_of(dfkv.dfkv_advance, geom(), requests(n_reqs=-3), outputs(), stream=0) == dfkv.DFKV_ERR_SHAPE
+    # the block placement needs the pool's page count: dfkv_advance refuses to place a block
+    assert status_of(dfkv.dfkv_advance, geom(), requests(), outputs(block_slot=addr(58)), stream=0) == \
+        dfkv.DFKV_ERR_SHAPE
+
+
+def test_block_placement_validation():
+    g = geom()
+    # block_slot over q_pos, over the block table, misaligned; no block table to place from
+    assert status_of(dfkv.dfkv_store_advance, g, addr(60), requests(), pool(), outputs(block_slot=addr(55) + 8),
+                     stream=0) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(dfkv.dfkv_store_advance, g, addr(60), requests(), pool(), outputs(block_slot=addr(24)),
+                     stream=0) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(dfkv.dfkv_store_advance, g, addr(60), requests(), pool(), outputs(block_slot=addr(58) + 4),
+                     stream=0) == dfkv.DFKV_ERR_LAYOUT
 
 
 def test_step_validation():
