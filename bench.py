@@ -130,6 +130,66 @@ def cpu_baseline(wl, seconds: float) -> dict:
                 us_per_step=1e6 * el / steps)
 
 
+def measure_overlap(ds, stream, R, per_graph, timed, n_rep, window_us) -> dict:
+    """The projection forked onto an aux stream ahead of a simulated sample/accept window (a spin kernel
+    of about `window_us` on the main stream) and joined before the store, against the same three pieces
+    in series on one stream (the overlap switch of the PR #20550 page).  Both captured in graphs of
+    `per_graph` consecutive steps rotating over the weight copies."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    aux = torch.cuda.Stream()
+    fork, join = torch.cuda.Event(), torch.cuda.Event()
+    fork.record(stream)
+    join.record(aux)
+    torch.cuda.synchronize()
+
+    def spin_cycles(us):
+        # calibrate the spin kernel's rate on this box (its clock is the shader clock)
+        with torch.cuda.stream(stream):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(1_000_000)
+            e0.record(stream)
+            torch.cuda._sleep(2_000_000)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        per_us = 2_000_000 / (e0.elapsed_time(e1) * 1e3)
+        return max(1, int(us * per_us))
+
+    cycles = spin_cycles(window_us)
+
+    def capture(body):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(per_graph):
+                body(i % R)
+        return g
+
+    def serial(c):
+        ds.project(copy=c, stream=stream)
+        torch.cuda._sleep(cycles)
+        ds.store_advance(stream=stream)
+
+    def overlapped(c):
+        ds.project_fork(stream, aux, fork.cuda_event, join.cuda_event, copy=c)
+        torch.cuda._sleep(cycles)
+        dfkv.dfkv_join(stream, join.cuda_event)
+        ds.store_advance(stream=stream)
+
+    def window_only(c):
+        torch.cuda._sleep(cycles)
+
+    g_ser, g_ovl, g_win = capture(serial), capture(overlapped), capture(window_only)
+    torch.cuda.synchronize()
+    reps = max(4, n_rep // 2)
+    ser = float(timed([g_ser], reps, 1, per_graph).mean())
+    ovl = float(timed([g_ovl], reps, 1, per_graph).mean())
+    win = float(timed([g_win], reps, 1, per_graph).mean())
+    return {"window_us": round(win, 2), "serial_us_per_step": round(ser, 2),
+            "overlapped_us_per_step": round(ovl, 2), "hidden_us_per_step": round(ser - ovl, 2),
+            "what": "project + simulated sample/accept window + store_advance per step; overlapped: the "
+                    "projection forked onto an aux stream ahead of the window, joined before the store"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +201,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated through (cache defeat)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-overlap", action="store_true", help="skip the overlapped-projection measurement")
+    ap.add_argument("--window-us", type=float, default=50.0,
+                    help="simulated sample/accept window the projection overlaps (us of spin on the main stream)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (for HBM counter scaling) and exit")
     args = ap.parse_args()
@@ -268,6 +331,8 @@ def main() -> int:
                     "TFLOP/s": round(alg["flops"] / (us_step * 1e-6) / 1e12, 2)}
     if staged_us is not None:
         roof["staged_path_us_per_step"] = round(float(staged_us.mean()), 2)
+    overlap = None if args.no_overlap else measure_overlap(ds, stream, R, STEPS_PER_GRAPH, timed, n_rep,
+                                                           args.window_us)
 
     out = {
         "metric": METRIC,
@@ -295,6 +360,8 @@ def main() -> int:
         "roofline": roof,
         "wall_s_timed": round(wall, 3),
     }
+    if overlap is not None:
+        out["overlap"] = overlap
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

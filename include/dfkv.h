@@ -330,6 +330,27 @@ dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfk
 dfkv_status dfkv_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
                                const dfkv_pool *pool, const dfkv_outputs *out, dfkv_stream_t stream);
 
+/* Overlapped context projection ([P20550] TLLM_DFLASH_OVERLAP_CONTEXT_PROJECTION:
+ * the gen tokens' context projection forks onto an aux stream ahead of
+ * sample/accept).  dfkv_project_fork validates exactly as dfkv_project, then
+ * records `fork` on `main` (so that everything already queued on main -- the
+ * target forward that produced `hidden` -- comes first), makes `aux` wait for
+ * it, queues the projection on `aux` and records `join` on `aux`.  The
+ * projection reads only the hidden states, the weights, the cos/sin cache and
+ * the pre-step ctx_len_in (never n_acc), so sample/accept may run on `main`
+ * meanwhile.  dfkv_join makes `main` wait for `join`: call it before anything
+ * on `main` reads kv_out or the workspace (dfkv_store_advance).  Streams and
+ * events (hipStream_t, hipEvent_t) are the caller's; both calls may be
+ * captured into one hipGraph together with the work on `main`.
+ * Errors: as dfkv_project (nothing queued, no event recorded); NULL for a NULL
+ * event; HIP when recording or waiting fails. */
+dfkv_status dfkv_project_fork(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
+                              int64_t hidden_row_stride, int32_t n_reqs, const int32_t *ctx_len_in,
+                              const float *cos_sin, int32_t cache_len, void *kv_out, uint32_t flags,
+                              void *ws, size_t ws_bytes, dfkv_stream_t main, dfkv_stream_t aux,
+                              void *fork, void *join);
+dfkv_status dfkv_join(dfkv_stream_t main, void *join);
+
 /* One whole step: dfkv_project(DFKV_FUSE_NORM_ROPE) into kv_out, then
  * dfkv_store_advance.  ctx_len_in is taken from req.  Errors as the parts. */
 dfkv_status dfkv_step(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,

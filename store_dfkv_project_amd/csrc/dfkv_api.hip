@@ -594,6 +594,30 @@ dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *
                        (flags & DFKV_FUSE_NORM_ROPE) != 0, ws, pl, fin, false, (hipStream_t)stream);
 }
 
+dfkv_status dfkv_project_fork(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
+                              int64_t hidden_row_stride, int32_t n_reqs, const int32_t *ctx_len_in,
+                              const float *cos_sin, int32_t cache_len, void *kv_out, uint32_t flags, void *ws,
+                              size_t ws_bytes, dfkv_stream_t main, dfkv_stream_t aux, void *fork, void *join) {
+    Plan pl;
+    dfkv_status st = check_project(g, w, hidden, hidden_row_stride, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out,
+                                   flags, ws, ws_bytes, &pl);
+    if (st != DFKV_OK) return st;
+    if (!fork || !join) return DFKV_ERR_NULL;
+    hipError_t e = hipEventRecord((hipEvent_t)fork, (hipStream_t)main);
+    if (e == hipSuccess) e = hipStreamWaitEvent((hipStream_t)aux, (hipEvent_t)fork, 0);
+    if (e != hipSuccess) return hip_status(e);
+    const FinalizeParams fin = fin_params(g, nullptr, nullptr, nullptr, n_reqs);
+    st = run_project(g, w, hidden, hidden_row_stride, ctx_len_in, cos_sin, cache_len, kv_out,
+                     (flags & DFKV_FUSE_NORM_ROPE) != 0, ws, pl, fin, false, (hipStream_t)aux);
+    if (st != DFKV_OK) return st;
+    return hip_status(hipEventRecord((hipEvent_t)join, (hipStream_t)aux));
+}
+
+dfkv_status dfkv_join(dfkv_stream_t main, void *join) {
+    if (!join) return DFKV_ERR_NULL;
+    return hip_status(hipStreamWaitEvent((hipStream_t)main, (hipEvent_t)join, 0));
+}
+
 dfkv_status dfkv_project_fc(const dfkv_geom *g, const void *w_fc, const void *w_hnorm, const void *hidden,
                             int64_t hidden_row_stride, int32_t n_reqs, void *ws, size_t ws_bytes,
                             dfkv_stream_t stream) {

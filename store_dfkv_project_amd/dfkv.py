@@ -34,7 +34,7 @@ DFKV_FUSE_NORM_ROPE = 1
 
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
-            "dfkv_store_advance", "dfkv_step")
+            "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join")
 
 
 class dfkv_geom(C.Structure):
@@ -113,6 +113,8 @@ def _load() -> C.CDLL:
         "dfkv_advance": ([gp, rp, op, P], C.c_int),
         "dfkv_store_advance": ([gp, P, rp, pp, op, P], C.c_int),
         "dfkv_step": ([gp, wp, P, I64, rp, P, I32, P, pp, op, P, SZ, P], C.c_int),
+        "dfkv_project_fork": ([gp, wp, P, I64, I32, P, P, I32, P, U32, P, SZ, P, P, P, P], C.c_int),
+        "dfkv_join": ([P, P], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -243,6 +245,19 @@ def dfkv_project(geom, weights, hidden, hidden_row_stride, n_reqs, ctx_len_in, c
     _check(_lib.dfkv_project(_ref(geom), _ref(weights), _ptr(hidden), int(hidden_row_stride), int(n_reqs),
                              _ptr(ctx_len_in), _ptr(cos_sin), int(cache_len), _ptr(kv_out), int(flags), _ptr(ws),
                              int(ws_bytes), _stream(stream)), "dfkv_project")
+
+
+def dfkv_project_fork(geom, weights, hidden, hidden_row_stride, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out,
+                      flags, ws, ws_bytes, main, aux, fork, join) -> None:
+    """`fork`/`join`: hipEvent_t handles (torch.cuda.Event.cuda_event after the event exists)."""
+    _check(_lib.dfkv_project_fork(_ref(geom), _ref(weights), _ptr(hidden), int(hidden_row_stride), int(n_reqs),
+                                  _ptr(ctx_len_in), _ptr(cos_sin), int(cache_len), _ptr(kv_out), int(flags),
+                                  _ptr(ws), int(ws_bytes), _stream(main), _stream(aux), C.c_void_p(fork),
+                                  C.c_void_p(join)), "dfkv_project_fork")
+
+
+def dfkv_join(main, join) -> None:
+    _check(_lib.dfkv_join(_stream(main), C.c_void_p(join)), "dfkv_join")
 
 
 def dfkv_project_fc(geom, w_fc, w_hnorm, hidden, hidden_row_stride, n_reqs, ws, ws_bytes, stream=None) -> None:

@@ -136,6 +136,13 @@ class DeviceStep:
                           self.ctx_len, self.cos_sin, self.cache_len, self.kv_out if kv_out is None else kv_out,
                           flags, self.ws, self.ws_bytes, stream)
 
+    def project_fork(self, main, aux, fork, join, flags: int = dfkv.DFKV_FUSE_NORM_ROPE, copy: int = 0):
+        """The projection on `aux` after the work queued on `main` so far; `join` recorded after it
+        (fork / join: raw hipEvent_t handles)."""
+        dfkv.dfkv_project_fork(self.gs, self.weight_structs[copy], self.hidden, self.wl.hidden_row_stride,
+                               self.wl.n_reqs, self.ctx_len, self.cos_sin, self.cache_len, self.kv_out, flags,
+                               self.ws, self.ws_bytes, main, aux, fork, join)
+
     def project_fc(self, copy: int = 0, stream=None):
         w = self.weights[copy]
         dfkv.dfkv_project_fc(self.gs, w[0], w[1], self.hidden, self.wl.hidden_row_stride, self.wl.n_reqs, self.ws,

@@ -241,6 +241,21 @@ def test_step_validation():
     assert status_of(dfkv.dfkv_step, **a) == dfkv.DFKV_ERR_LAYOUT
 
 
+def test_fork_join_validation():
+    """The overlapped projection validates as dfkv_project before touching any stream or event."""
+    g = geom()
+    ws = dfkv.dfkv_workspace_size(g, 2)
+    w = dfkv.make_weights(addr(1), addr(2), addr(3), addr(4))
+    base = dict(geom=g, weights=w, hidden=addr(5), hidden_row_stride=12288, n_reqs=2, ctx_len_in=addr(6),
+                cos_sin=addr(7), cache_len=4096, kv_out=addr(8), flags=1, ws=addr(9), ws_bytes=ws, main=0, aux=0,
+                fork=addr(11), join=addr(12))
+    assert status_of(dfkv.dfkv_project_fork, **dict(base, fork=0)) == dfkv.DFKV_ERR_NULL
+    assert status_of(dfkv.dfkv_project_fork, **dict(base, join=0)) == dfkv.DFKV_ERR_NULL
+    assert status_of(dfkv.dfkv_project_fork, **dict(base, ws_bytes=ws - 256)) == dfkv.DFKV_ERR_WORKSPACE
+    assert status_of(dfkv.dfkv_project_fork, **dict(base, kv_out=addr(5))) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(dfkv.dfkv_join, 0, 0) == dfkv.DFKV_ERR_NULL
+
+
 def test_rope_cache_validation():
     r = dfkv.make_rope(1e6, 64)
     assert status_of(dfkv.dfkv_rope_cache_build, dfkv.make_rope(1e6, 63), addr(7), 10, stream=0) == \
