@@ -75,9 +75,11 @@ class Oracle:
                                               _P, _I64, _I64, C.c_int32, _P, _P, _P, _P, _P, _P, _P, _P]
         L.dfkv_oracle_store.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64, _I64, _I64]
         L.dfkv_oracle_block_placement.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I64, _I, _I, _P]
+        L.dfkv_oracle_block_table_decode.argtypes = [_I, _I, _P, _I64, _I64, _P, _I, _I, _P, _P, _I64]
         for fn in ("dfkv_oracle_linear", "dfkv_oracle_rmsnorm", "dfkv_oracle_inv_freq", "dfkv_oracle_rope_cache",
                    "dfkv_oracle_rope_neox", "dfkv_oracle_norm_rope", "dfkv_oracle_project",
-                   "dfkv_oracle_bookkeeping", "dfkv_oracle_store", "dfkv_oracle_block_placement"):
+                   "dfkv_oracle_bookkeeping", "dfkv_oracle_store", "dfkv_oracle_block_placement",
+                   "dfkv_oracle_block_table_decode"):
             getattr(L, fn).restype = None
         self.lib = L
 
@@ -219,6 +221,19 @@ class Oracle:
         self.lib.dfkv_oracle_block_placement(B, bs, geom.page_size, *[_ptr(a) for a in ins], _ptr(bt), bt_stride,
                                              bt_cols, num_pages, _ptr(out))
         return out.reshape(B, bs)
+
+    def block_table_decode(self, offsets_buf: np.ndarray, s_req: int, s_blk: int, n_reqs: int, max_blocks: int,
+                           n_tokens, page_size: int, divisor: int):
+        """Draft-KV block-table decode (PR #20550 page: page counts and the decoded table; clamped and divided
+        offsets).  `offsets_buf` is the storage of a strided view: element (r, b) at r*s_req + b*s_blk.
+        Returns (page_count [B] int32, table [B, max_blocks] int32)."""
+        buf = np.ascontiguousarray(offsets_buf, dtype=np.int32)
+        cnt = np.empty(n_reqs, np.int32)
+        tbl = np.empty((n_reqs, max_blocks), np.int32)
+        nt = np.ascontiguousarray(n_tokens, dtype=np.int32)
+        self.lib.dfkv_oracle_block_table_decode(n_reqs, max_blocks, _ptr(buf), s_req, s_blk, _ptr(nt), page_size,
+                                                divisor, _ptr(cnt), _ptr(tbl), max_blocks)
+        return cnt, tbl
 
     def store(self, geom, kv: np.ndarray, slot: np.ndarray, write_mask: np.ndarray, pools_k: Sequence[np.ndarray],
               pools_v: Optional[Sequence[np.ndarray]], s_page: int, s_slot: int, s_head: int) -> None:

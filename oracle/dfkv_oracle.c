@@ -433,6 +433,39 @@ EXPORT void dfkv_oracle_block_placement(int B, int bs_blk, int pg, const int32_t
 }
 
 /* ------------------------------------------------------------------------ */
+/* Draft-KV block-table decode (PR #20550 page: the refresh of the draft      */
+/* block table, "page counts and decoded table"; downstream commit: the       */
+/* decode of blocks per request with clamped and divided offsets, checked on  */
+/* a strided view of the offsets tensor, an all-negative row, an all-zero row */
+/* and about half negative or zero entries).  Reading: request r holds        */
+/* n_tokens[r] tokens of draft context; offsets[r][b] counts in units of      */
+/* 1/divisor page (negative: no page).                                        */
+/*   page_count[r] = clamp(ceil(n_tokens[r] / page_size), 0, max_blocks)      */
+/*   table[r][b]   = b < page_count[r] && offsets[r][b] >= 0                  */
+/*                   ? offsets[r][b] / divisor : -1                           */
+/* ------------------------------------------------------------------------ */
+
+EXPORT void dfkv_oracle_block_table_decode(int B, int max_blocks, const int32_t *offsets, int64_t s_req,
+                                           int64_t s_blk, const int32_t *n_tokens, int page_size, int divisor,
+                                           int32_t *page_count_out, int32_t *table_out, int64_t t_stride)
+{
+    for (int r = 0; r < B; ++r) {
+        int64_t n = n_tokens[r];
+        int64_t pages = n <= 0 ? 0 : (n + page_size - 1) / page_size;
+#if DFKV_ORACLE_MUTANT == 9 /* planted: pages rounded down */
+        pages = n <= 0 ? 0 : n / page_size;
+#endif
+        if (pages > max_blocks)
+            pages = max_blocks;
+        page_count_out[r] = (int32_t)pages;
+        for (int b = 0; b < max_blocks; ++b) {
+            int32_t off = offsets[(int64_t)r * s_req + (int64_t)b * s_blk];
+            table_out[(int64_t)r * t_stride + b] = (b < pages && off >= 0) ? off / divisor : -1;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Paged store: every written row goes into every layer's pool.              */
 /* GQA: layer l's K pool gets kv[row][l][0][h][:] at                         */
 /*      page*s_page + off*s_slot + h*s_head, its V pool kv[row][l][1][h][:]. */

@@ -566,6 +566,61 @@ def pin_golden_block_placement(o):
 
 
 # ---------------------------------------------------------------------------
+# draft-KV block-table decode
+# ---------------------------------------------------------------------------
+
+def pin_block_table_decode_position_walk(o):
+    """Page counts from a walk over token positions (the distinct pages that positions 0..n-1 fall in,
+    at most the table's width); each kept entry t is the page whose divisor-wide offset range holds the
+    offset (t*d <= off < (t+1)*d); negative offsets and blocks past the count give -1."""
+    rng = np.random.default_rng(65)
+    for _ in range(300):
+        B, mb = int(rng.integers(1, 6)), int(rng.integers(0, 7))
+        pg, d = int(rng.integers(1, 9)), int(rng.integers(1, 5))
+        off = rng.integers(-3, 40, size=(B, mb)).astype(np.int32)
+        off[rng.random((B, mb)) < 0.3] = 0
+        n_tok = rng.integers(-3, pg * (mb + 2) + 2, size=B).astype(np.int32)
+        cnt, tbl = o.block_table_decode(off, mb, 1, B, mb, n_tok, pg, d)
+        for r in range(B):
+            walk = len({p // pg for p in range(max(0, int(n_tok[r])))})
+            assert cnt[r] == min(walk, mb), (r, cnt[r], walk)
+            for b in range(mb):
+                t, v = int(tbl[r, b]), int(off[r, b])
+                if b >= cnt[r] or v < 0:
+                    assert t == -1, (r, b, t)
+                else:
+                    assert t >= 0 and t * d <= v < (t + 1) * d, (r, b, t, v, d)
+
+
+def pin_block_table_decode_strided_views(o):
+    """The offsets may be any strided view: row-major, transposed and every-other-column storage of one
+    logical table decode identically."""
+    rng = np.random.default_rng(66)
+    B, mb = 7, 9
+    off = rng.integers(-4, 50, size=(B, mb)).astype(np.int32)
+    n_tok = rng.integers(0, 60, size=B).astype(np.int32)
+    a = o.block_table_decode(off, mb, 1, B, mb, n_tok, 8, 3)
+    b = o.block_table_decode(np.ascontiguousarray(off.T), 1, B, B, mb, n_tok, 8, 3)
+    wide = np.full((B, 2 * mb), 12345, np.int32)
+    wide[:, ::2] = off
+    c = o.block_table_decode(wide, 2 * mb, 2, B, mb, n_tok, 8, 3)
+    for x in (b, c):
+        assert np.array_equal(a[0], x[0]) and np.array_equal(a[1], x[1])
+
+
+def pin_golden_block_table_decode(o):
+    """A case worked by hand (tests/golden/block_table_decode_tiny.json)."""
+    with open(os.path.join(GOLDEN, "block_table_decode_tiny.json")) as fh:
+        g = json.load(fh)
+    i = g["inputs"]
+    cnt, tbl = o.block_table_decode(np.array(i["offsets_storage"], np.int32), i["stride_req"], i["stride_blk"],
+                                    g["n_reqs"], g["max_blocks"], np.array(i["n_tokens"], np.int32), g["page_size"],
+                                    g["divisor"])
+    assert np.array_equal(cnt, np.array(g["expected"]["page_count"])), cnt
+    assert np.array_equal(tbl, np.array(g["expected"]["table"])), tbl
+
+
+# ---------------------------------------------------------------------------
 # paged store
 # ---------------------------------------------------------------------------
 
