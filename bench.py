@@ -190,6 +190,31 @@ def measure_overlap(ds, stream, R, per_graph, timed, n_rep, window_us) -> dict:
                     "projection forked onto an aux stream ahead of the window, joined before the store"}
 
 
+def measure_bt_decode(stream, timed, B: int = 256, max_blocks: int = 1024) -> dict:
+    """dfkv_block_table_decode on a serving-sized table (256 requests x 1024 blocks, transposed offsets
+    view, about half the entries negative or zero), 20 launches per captured graph."""
+    import numpy as np
+    import torch
+    from store_dfkv_project_amd import dfkv
+    rng = np.random.default_rng(7)
+    off = rng.integers(0, 1 << 20, size=(B, max_blocks)).astype(np.int32)
+    off[rng.random((B, max_blocks)) < 0.5] = -1
+    buf = torch.from_numpy(np.ascontiguousarray(off.T)).cuda()
+    n_tok = torch.from_numpy(rng.integers(0, 64 * max_blocks, size=B).astype(np.int32)).cuda()
+    cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+    tbl = torch.zeros((B, max_blocks), dtype=torch.int32, device="cuda")
+    per = 20
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(per):
+            dfkv.dfkv_block_table_decode(buf, 1, B, B, max_blocks, n_tok, 64, 2, cnt, tbl, max_blocks, stream)
+    torch.cuda.synchronize()
+    us = float(timed([g], 20, 2, per).mean())
+    nbytes = 2 * 4 * B * max_blocks + 8 * B
+    return {"requests": B, "max_blocks": max_blocks, "us_per_launch": round(us, 2),
+            "bytes_per_launch": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -333,6 +358,7 @@ def main() -> int:
         roof["staged_path_us_per_step"] = round(float(staged_us.mean()), 2)
     overlap = None if args.no_overlap else measure_overlap(ds, stream, R, STEPS_PER_GRAPH, timed, n_rep,
                                                            args.window_us)
+    bt_decode = measure_bt_decode(stream, timed)
 
     out = {
         "metric": METRIC,
@@ -362,6 +388,7 @@ def main() -> int:
     }
     if overlap is not None:
         out["overlap"] = overlap
+    out["block_table_decode"] = bt_decode
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

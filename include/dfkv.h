@@ -330,6 +330,26 @@ dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfk
 dfkv_status dfkv_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
                                const dfkv_pool *pool, const dfkv_outputs *out, dfkv_stream_t stream);
 
+/* Draft-KV block-table decode ([P20550]: the refresh of the draft block table,
+ * "page counts and decoded table"; downstream commit: the decode of blocks per
+ * request with clamped and divided offsets is one launch).  Request r holds
+ * n_tokens[r] tokens of draft context; offsets element (r, b) is at
+ * r*off_stride_req + b*off_stride_blk (any strided view, e.g. a transposed
+ * tensor; int32, counting in units of 1/divisor page, negative = no page).
+ *   page_count[r] = clamp(ceil(n_tokens[r] / page_size), 0, max_blocks)
+ *   table[r][b]   = b < page_count[r] && offsets(r, b) >= 0
+ *                   ? offsets(r, b) / divisor : -1       (b < max_blocks)
+ * table row r starts at table_out + r*table_row_stride (int32); the result is
+ * a block table for dfkv_requests (bt_row_stride = table_row_stride,
+ * bt_cols = max_blocks).  One launch; no value is read out of bounds.
+ * Errors: NULL; SHAPE (n_reqs, max_blocks < 0; page_size, divisor <= 0);
+ * LAYOUT (negative offset strides, table_row_stride < max_blocks); ALIAS
+ * (outputs overlapping each other or the inputs); HIP. */
+dfkv_status dfkv_block_table_decode(const int32_t *offsets, int64_t off_stride_req, int64_t off_stride_blk,
+                                    int32_t n_reqs, int32_t max_blocks, const int32_t *n_tokens,
+                                    int32_t page_size, int32_t divisor, int32_t *page_count_out,
+                                    int32_t *table_out, int64_t table_row_stride, dfkv_stream_t stream);
+
 /* Overlapped context projection ([P20550] TLLM_DFLASH_OVERLAP_CONTEXT_PROJECTION:
  * the gen tokens' context projection forks onto an aux stream ahead of
  * sample/accept).  dfkv_project_fork validates exactly as dfkv_project, then

@@ -613,6 +613,27 @@ dfkv_status dfkv_project_fork(const dfkv_geom *g, const dfkv_weights *w, const v
     return hip_status(hipEventRecord((hipEvent_t)join, (hipStream_t)aux));
 }
 
+dfkv_status dfkv_block_table_decode(const int32_t *offsets, int64_t off_stride_req, int64_t off_stride_blk,
+                                    int32_t n_reqs, int32_t max_blocks, const int32_t *n_tokens, int32_t page_size,
+                                    int32_t divisor, int32_t *page_count_out, int32_t *table_out,
+                                    int64_t table_row_stride, dfkv_stream_t stream) {
+    if (n_reqs < 0 || max_blocks < 0 || page_size <= 0 || divisor <= 0) return DFKV_ERR_SHAPE;
+    if (n_reqs == 0) return DFKV_OK;
+    if (!n_tokens || !page_count_out || (max_blocks > 0 && (!offsets || !table_out))) return DFKV_ERR_NULL;
+    if (off_stride_req < 0 || off_stride_blk < 0 || table_row_stride < max_blocks) return DFKV_ERR_LAYOUT;
+    const int64_t B = n_reqs;
+    const size_t off_b = max_blocks > 0 ? extent2(off_stride_req, B, off_stride_blk, max_blocks) : 0;
+    const size_t tbl_b = max_blocks > 0 ? (size_t)((B - 1) * table_row_stride + max_blocks) * 4 : 0;
+    const size_t cnt_b = (size_t)B * 4, nt_b = (size_t)B * 4;
+    if (overlap(page_count_out, cnt_b, n_tokens, nt_b) || overlap(page_count_out, cnt_b, offsets, off_b) ||
+        overlap(table_out, tbl_b, n_tokens, nt_b) || overlap(table_out, tbl_b, offsets, off_b) ||
+        overlap(table_out, tbl_b, page_count_out, cnt_b))
+        return DFKV_ERR_ALIAS;
+    BtDecodeArgs a{offsets, off_stride_req, off_stride_blk, n_tokens, n_reqs, max_blocks, page_size, divisor,
+                   page_count_out, table_out, table_row_stride};
+    return hip_status(launch_bt_decode(a, (hipStream_t)stream));
+}
+
 dfkv_status dfkv_join(dfkv_stream_t main, void *join) {
     if (!join) return DFKV_ERR_NULL;
     return hip_status(hipStreamWaitEvent((hipStream_t)main, (hipEvent_t)join, 0));

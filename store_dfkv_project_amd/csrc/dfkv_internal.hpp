@@ -108,6 +108,17 @@ struct FinalizeParams {
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s);
 hipError_t launch_advance(const FinalizeParams &p, hipStream_t s);
 
+// Draft-KV block-table decode (k_misc.hip)
+struct BtDecodeArgs {
+    const int32_t *off;
+    int64_t s_req, s_blk;
+    const int32_t *n_tokens;
+    int32_t B, max_blocks, page_size, divisor;
+    int32_t *count, *table;
+    int64_t t_stride;
+};
+hipError_t launch_bt_decode(const BtDecodeArgs &a, hipStream_t s);
+
 // part != null: f = bf16(sum of the S fp32 partials [S][n_rows][H]) is formed and written first
 hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint16_t *w, uint16_t *g, int n_rows,
                               int H, float eps, hipStream_t s);

@@ -159,3 +159,46 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
 }
 
 }  // namespace dfkv
+
+namespace dfkv {
+
+// ---------------------------------------------------------------------------
+// Draft-KV block-table decode (TensorRT-LLM PR #20550 "fuse the decode-step
+// drafter bookkeeping into Triton kernels": the refresh of the draft block
+// table, page counts and decoded table; the downstream commit quoted on that
+// page: blocks per request, clamped and divided offsets, one launch).
+//   count[r]    = clamp(ceil(n_tokens[r] / page_size), 0, max_blocks)
+//   table[r][b] = b < count[r] && off(r, b) >= 0 ? off(r, b) / divisor : -1
+// One thread per table entry; the entries of a row are consecutive threads, so
+// the table stores coalesce (the strided offset view need not).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bt_decode(const BtDecodeArgs a) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (int64_t)a.B * a.max_blocks) return;
+    const int r = (int)(e / a.max_blocks), b = (int)(e - (int64_t)r * a.max_blocks);
+    const int64_t n = a.n_tokens[r];
+    int64_t pages = n <= 0 ? 0 : (n + a.page_size - 1) / a.page_size;
+    pages = pages < a.max_blocks ? pages : a.max_blocks;
+    if (b == 0) a.count[r] = (int32_t)pages;
+    int32_t t = -1;
+    if (b < pages) {
+        const int32_t off = a.off[(int64_t)r * a.s_req + (int64_t)b * a.s_blk];
+        if (off >= 0) t = off / a.divisor;
+    }
+    a.table[(int64_t)r * a.t_stride + b] = t;
+}
+
+// rows with no blocks still get their page count
+__global__ __launch_bounds__(256) void k_bt_count(const BtDecodeArgs a) {
+    const int r = blockIdx.x * 256 + threadIdx.x;
+    if (r < a.B) a.count[r] = 0;
+}
+
+hipError_t launch_bt_decode(const BtDecodeArgs &a, hipStream_t s) {
+    if (a.B <= 0) return hipSuccess;
+    if (a.max_blocks == 0) return launch1(k_bt_count, dim3((unsigned)((a.B + 255) / 256)), dim3(256), s, a);
+    const int64_t n = (int64_t)a.B * a.max_blocks;
+    return launch1(k_bt_decode, dim3((unsigned)((n + 255) / 256)), dim3(256), s, a);
+}
+
+}  // namespace dfkv

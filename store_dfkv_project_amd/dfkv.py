@@ -34,7 +34,7 @@ DFKV_FUSE_NORM_ROPE = 1
 
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
-            "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join")
+            "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join", "dfkv_block_table_decode")
 
 
 class dfkv_geom(C.Structure):
@@ -115,6 +115,7 @@ def _load() -> C.CDLL:
         "dfkv_step": ([gp, wp, P, I64, rp, P, I32, P, pp, op, P, SZ, P], C.c_int),
         "dfkv_project_fork": ([gp, wp, P, I64, I32, P, P, I32, P, U32, P, SZ, P, P, P, P], C.c_int),
         "dfkv_join": ([P, P], C.c_int),
+        "dfkv_block_table_decode": ([P, I64, I64, I32, I32, P, I32, I32, P, P, I64, P], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -254,6 +255,14 @@ def dfkv_project_fork(geom, weights, hidden, hidden_row_stride, n_reqs, ctx_len_
                                   _ptr(ctx_len_in), _ptr(cos_sin), int(cache_len), _ptr(kv_out), int(flags),
                                   _ptr(ws), int(ws_bytes), _stream(main), _stream(aux), C.c_void_p(fork),
                                   C.c_void_p(join)), "dfkv_project_fork")
+
+
+def dfkv_block_table_decode(offsets, off_stride_req, off_stride_blk, n_reqs, max_blocks, n_tokens, page_size,
+                            divisor, page_count_out, table_out, table_row_stride, stream=None) -> None:
+    _check(_lib.dfkv_block_table_decode(_ptr(offsets), int(off_stride_req), int(off_stride_blk), int(n_reqs),
+                                        int(max_blocks), _ptr(n_tokens), int(page_size), int(divisor),
+                                        _ptr(page_count_out), _ptr(table_out), int(table_row_stride),
+                                        _stream(stream)), "dfkv_block_table_decode")
 
 
 def dfkv_join(main, join) -> None:

@@ -256,6 +256,21 @@ def test_fork_join_validation():
     assert status_of(dfkv.dfkv_join, 0, 0) == dfkv.DFKV_ERR_NULL
 
 
+def test_block_table_decode_validation():
+    f = dfkv.dfkv_block_table_decode
+    base = dict(offsets=addr(1), off_stride_req=8, off_stride_blk=1, n_reqs=4, max_blocks=8, n_tokens=addr(2),
+                page_size=64, divisor=2, page_count_out=addr(3), table_out=addr(4), table_row_stride=8, stream=0)
+    assert status_of(f, **dict(base, divisor=0)) == dfkv.DFKV_ERR_SHAPE
+    assert status_of(f, **dict(base, page_size=0)) == dfkv.DFKV_ERR_SHAPE
+    assert status_of(f, **dict(base, max_blocks=-1)) == dfkv.DFKV_ERR_SHAPE
+    assert status_of(f, **dict(base, n_tokens=None)) == dfkv.DFKV_ERR_NULL
+    assert status_of(f, **dict(base, table_row_stride=7)) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(f, **dict(base, off_stride_blk=-1)) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(f, **dict(base, table_out=addr(1) + 64)) == dfkv.DFKV_ERR_ALIAS   # table over the offsets
+    assert status_of(f, **dict(base, page_count_out=addr(4) + 16)) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(f, **dict(base, n_reqs=0, offsets=None, n_tokens=None)) == dfkv.DFKV_OK
+
+
 def test_rope_cache_validation():
     r = dfkv.make_rope(1e6, 64)
     assert status_of(dfkv.dfkv_rope_cache_build, dfkv.make_rope(1e6, 63), addr(7), 10, stream=0) == \
