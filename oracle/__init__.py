@@ -76,10 +76,11 @@ class Oracle:
         L.dfkv_oracle_store.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I64, _I64, _I64]
         L.dfkv_oracle_block_placement.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I64, _I, _I, _P]
         L.dfkv_oracle_block_table_decode.argtypes = [_I, _I, _P, _I64, _I64, _P, _I, _I, _P, _P, _I64]
+        L.dfkv_oracle_strict_accept.argtypes = [_I, _I, _P, _I64, _I64, _P, _I64, _I64, _P, _P]
         for fn in ("dfkv_oracle_linear", "dfkv_oracle_rmsnorm", "dfkv_oracle_inv_freq", "dfkv_oracle_rope_cache",
                    "dfkv_oracle_rope_neox", "dfkv_oracle_norm_rope", "dfkv_oracle_project",
                    "dfkv_oracle_bookkeeping", "dfkv_oracle_store", "dfkv_oracle_block_placement",
-                   "dfkv_oracle_block_table_decode"):
+                   "dfkv_oracle_block_table_decode", "dfkv_oracle_strict_accept"):
             getattr(L, fn).restype = None
         self.lib = L
 
@@ -234,6 +235,18 @@ class Oracle:
         self.lib.dfkv_oracle_block_table_decode(n_reqs, max_blocks, _ptr(buf), s_req, s_blk, _ptr(nt), page_size,
                                                 divisor, _ptr(cnt), _ptr(tbl), max_blocks)
         return cnt, tbl
+
+    def strict_accept(self, target_buf, t_sr: int, t_st: int, draft_buf, d_sr: int, d_st: int, n_reqs: int,
+                      width: int):
+        """Strict acceptance of a uniform-width draft (the downstream commit quoted on the PR #20550 page).
+        Returns (n_acc [B] int32, accepted [B, width] int32 = the target's tokens)."""
+        t = np.ascontiguousarray(target_buf, dtype=np.int32)
+        d = np.ascontiguousarray(draft_buf, dtype=np.int32)
+        n_acc = np.empty(n_reqs, np.int32)
+        acc = np.empty((n_reqs, width), np.int32)
+        self.lib.dfkv_oracle_strict_accept(n_reqs, width, _ptr(t), t_sr, t_st, _ptr(d), d_sr, d_st, _ptr(n_acc),
+                                           _ptr(acc))
+        return n_acc, acc
 
     def store(self, geom, kv: np.ndarray, slot: np.ndarray, write_mask: np.ndarray, pools_k: Sequence[np.ndarray],
               pools_v: Optional[Sequence[np.ndarray]], s_page: int, s_slot: int, s_head: int) -> None:

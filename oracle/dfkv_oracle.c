@@ -466,6 +466,37 @@ EXPORT void dfkv_oracle_block_table_decode(int B, int max_blocks, const int32_t 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Strict acceptance of a uniform-width draft (the downstream commit quoted  */
+/* on the PR #20550 page: strict acceptance of a uniform-width draft is one  */
+/* launch; ragged verification keeps its path).  Request r verified W = K+1  */
+/* tokens: the target's token at each of the W positions, target[r][i], and  */
+/* the K drafted tokens draft[r][i].  The draft is accepted up to its first  */
+/* mismatch, and the target's token after the last accepted draft token is   */
+/* the bonus:                                                                */
+/*   n_acc[r]       = 1 + max{ m <= K : draft[r][i] == target[r][i], i < m } */
+/*   accepted[r][i] = target[r][i], i < W   (the first n_acc[r] are valid)   */
+/* ------------------------------------------------------------------------ */
+
+EXPORT void dfkv_oracle_strict_accept(int B, int W, const int32_t *target, int64_t t_sr, int64_t t_st,
+                                      const int32_t *draft, int64_t d_sr, int64_t d_st, int32_t *n_acc_out,
+                                      int32_t *accepted_out)
+{
+    for (int r = 0; r < B; ++r) {
+        int m = 0;
+        while (m < W - 1 && draft[(int64_t)r * d_sr + (int64_t)m * d_st] ==
+                                target[(int64_t)r * t_sr + (int64_t)m * t_st])
+            ++m;
+#if DFKV_ORACLE_MUTANT == 10 /* planted: the bonus token not counted */
+        n_acc_out[r] = m;
+#else
+        n_acc_out[r] = 1 + m;
+#endif
+        for (int i = 0; i < W; ++i)
+            accepted_out[(int64_t)r * W + i] = target[(int64_t)r * t_sr + (int64_t)i * t_st];
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Paged store: every written row goes into every layer's pool.              */
 /* GQA: layer l's K pool gets kv[row][l][0][h][:] at                         */
 /*      page*s_page + off*s_slot + h*s_head, its V pool kv[row][l][1][h][:]. */

@@ -621,6 +621,55 @@ def pin_golden_block_table_decode(o):
 
 
 # ---------------------------------------------------------------------------
+# strict acceptance of a uniform-width draft
+# ---------------------------------------------------------------------------
+
+def pin_strict_accept_prefix_search(o):
+    """n_acc - 1 is the longest m such that the first m drafted tokens all equal the target's (found by trying
+    every m from the longest down); the accepted tokens are the target's; 1 <= n_acc <= W."""
+    rng = np.random.default_rng(67)
+    for _ in range(400):
+        B, W = int(rng.integers(1, 7)), int(rng.integers(1, 7))
+        tgt = rng.integers(0, 3, size=(B, W)).astype(np.int32)          # tiny vocabulary: many matches
+        drf = rng.integers(0, 3, size=(B, max(W - 1, 0))).astype(np.int32)
+        n_acc, acc = o.strict_accept(tgt, W, 1, drf, max(W - 1, 1), 1, B, W)
+        assert np.array_equal(acc, tgt)
+        for r in range(B):
+            best = next(m for m in range(W - 1, -1, -1) if all(drf[r, i] == tgt[r, i] for i in range(m)))
+            assert n_acc[r] == best + 1 and 1 <= n_acc[r] <= W, (r, n_acc[r], best)
+
+
+def pin_golden_strict_accept(o):
+    """A case worked by hand (tests/golden/strict_accept_tiny.json), target stored transposed."""
+    with open(os.path.join(GOLDEN, "strict_accept_tiny.json")) as fh:
+        g = json.load(fh)
+    i, W, B = g["inputs"], g["width"], g["n_reqs"]
+    n_acc, acc = o.strict_accept(np.array(i["target_storage"], np.int32), i["t_stride_req"], i["t_stride_tok"],
+                                 np.array(i["draft"], np.int32), W - 1, 1, B, W)
+    assert np.array_equal(n_acc, np.array(g["expected"]["n_acc"])), n_acc
+    assert np.array_equal(acc, np.array(g["expected"]["accepted"])), acc
+
+
+def pin_strict_accept_feeds_bookkeeping(o):
+    """Acceptance then bookkeeping: the bonus token is the target's token after the last accepted draft
+    token, i.e. target[r][n_acc - 1]."""
+    rng = np.random.default_rng(68)
+    geom = Geometry(kind=GQA, n_tgt=1, tgt_hidden=8, hidden=8, n_layers=1, n_kv_heads=1, head_dim=8, latent_dim=0,
+                    rope_dim=8, eps=1e-6, page_size=4, width=5, block_size=3)
+    B, W = 9, 5
+    tgt = rng.integers(0, 2, size=(B, W)).astype(np.int32)
+    drf = np.where(rng.random((B, W - 1)) < 0.7, tgt[:, :W - 1], 1 - tgt[:, :W - 1]).astype(np.int32)
+    n_acc, acc = o.strict_accept(tgt, W, 1, drf, W - 1, 1, B, W)
+    tbl = np.arange(B * 4, dtype=np.int32).reshape(B, 4)
+    out = o.bookkeeping(geom, B, np.zeros(B, np.int32), n_acc, np.full(B, 16, np.int32), np.zeros(B, np.uint8),
+                        None, tbl, acc, W, 1, 77, 64)
+    for r in range(B):
+        first_miss = next((i for i in range(W - 1) if drf[r, i] != tgt[r, i]), W - 1)
+        assert out["bonus"][r] == tgt[r, first_miss]
+        assert out["ctx_len"][r] == n_acc[r]
+
+
+# ---------------------------------------------------------------------------
 # paged store
 # ---------------------------------------------------------------------------
 
