@@ -215,6 +215,29 @@ def measure_bt_decode(stream, timed, B: int = 256, max_blocks: int = 1024) -> di
             "bytes_per_launch": nbytes, "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
+def measure_accept(stream, timed, B: int = 256, W: int = 16) -> dict:
+    """dfkv_strict_accept at the stress batch (256 requests x 16 verified tokens, transposed target view),
+    20 launches per captured graph."""
+    import numpy as np
+    import torch
+    from store_dfkv_project_amd import dfkv
+    rng = np.random.default_rng(8)
+    tgt = rng.integers(0, 151936, size=(B, W)).astype(np.int32)
+    drf = np.where(rng.random((B, W - 1)) < 0.8, tgt[:, :W - 1], 0).astype(np.int32)
+    td = torch.from_numpy(np.ascontiguousarray(tgt.T)).cuda()
+    dd = torch.from_numpy(drf).cuda()
+    n_acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    acc = torch.zeros((B, W), dtype=torch.int32, device="cuda")
+    per = 20
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(per):
+            dfkv.dfkv_strict_accept(td, 1, B, dd, W - 1, 1, B, W, n_acc, acc, stream)
+    torch.cuda.synchronize()
+    us = float(timed([g], 20, 2, per).mean())
+    return {"requests": B, "width": W, "us_per_launch": round(us, 2)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -359,6 +382,7 @@ def main() -> int:
     overlap = None if args.no_overlap else measure_overlap(ds, stream, R, STEPS_PER_GRAPH, timed, n_rep,
                                                            args.window_us)
     bt_decode = measure_bt_decode(stream, timed)
+    accept = measure_accept(stream, timed)
 
     out = {
         "metric": METRIC,
@@ -389,6 +413,7 @@ def main() -> int:
     if overlap is not None:
         out["overlap"] = overlap
     out["block_table_decode"] = bt_decode
+    out["strict_accept"] = accept
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

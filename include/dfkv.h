@@ -330,6 +330,24 @@ dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfk
 dfkv_status dfkv_store_advance(const dfkv_geom *g, const void *kv, const dfkv_requests *req,
                                const dfkv_pool *pool, const dfkv_outputs *out, dfkv_stream_t stream);
 
+/* Strict acceptance of a uniform-width draft ([P20550] downstream commit:
+ * strict acceptance of a uniform-width draft is one launch; ragged
+ * verification keeps its path).  Request r verified W = width = K+1 tokens:
+ * target element (r, i), i < W, at r*t_stride_req + i*t_stride_tok is the
+ * target's token at verify position i; draft element (r, i), i < K, at
+ * r*d_stride_req + i*d_stride_tok is the i-th drafted token (any strided
+ * views; int32).  The draft is accepted up to its first mismatch and the
+ * target's token after it is the bonus:
+ *   n_acc[r]          = 1 + max{ m <= K : draft(r, i) == target(r, i), i < m }
+ *   accepted[r*W + i] = target(r, i)   (the first n_acc[r] are the accepted ones)
+ * n_acc and accepted feed dfkv_requests (acc_stride_req = W, acc_stride_tok = 1).
+ * Errors: NULL; SHAPE (n_reqs < 0, width < 1); LAYOUT (negative strides);
+ * ALIAS (outputs overlapping each other or the inputs); HIP. */
+dfkv_status dfkv_strict_accept(const int32_t *target, int64_t t_stride_req, int64_t t_stride_tok,
+                               const int32_t *draft, int64_t d_stride_req, int64_t d_stride_tok,
+                               int32_t n_reqs, int32_t width, int32_t *n_acc_out, int32_t *accepted_out,
+                               dfkv_stream_t stream);
+
 /* Draft-KV block-table decode ([P20550]: the refresh of the draft block table,
  * "page counts and decoded table"; downstream commit: the decode of blocks per
  * request with clamped and divided offsets is one launch).  Request r holds

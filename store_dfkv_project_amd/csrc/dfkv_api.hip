@@ -634,6 +634,26 @@ dfkv_status dfkv_block_table_decode(const int32_t *offsets, int64_t off_stride_r
     return hip_status(launch_bt_decode(a, (hipStream_t)stream));
 }
 
+dfkv_status dfkv_strict_accept(const int32_t *target, int64_t t_stride_req, int64_t t_stride_tok,
+                               const int32_t *draft, int64_t d_stride_req, int64_t d_stride_tok, int32_t n_reqs,
+                               int32_t width, int32_t *n_acc_out, int32_t *accepted_out, dfkv_stream_t stream) {
+    if (n_reqs < 0 || width < 1) return DFKV_ERR_SHAPE;
+    if (n_reqs == 0) return DFKV_OK;
+    if (!target || !n_acc_out || !accepted_out || (width > 1 && !draft)) return DFKV_ERR_NULL;
+    if (t_stride_req < 0 || t_stride_tok < 0 || d_stride_req < 0 || d_stride_tok < 0) return DFKV_ERR_LAYOUT;
+    const int64_t B = n_reqs;
+    const size_t t_b = extent2(t_stride_req, B, t_stride_tok, width);
+    const size_t d_b = width > 1 ? extent2(d_stride_req, B, d_stride_tok, width - 1) : 0;
+    const size_t n_b = (size_t)B * 4, a_b = (size_t)(B * width) * 4;
+    if (overlap(n_acc_out, n_b, target, t_b) || overlap(n_acc_out, n_b, draft, d_b) ||
+        overlap(accepted_out, a_b, target, t_b) || overlap(accepted_out, a_b, draft, d_b) ||
+        overlap(accepted_out, a_b, n_acc_out, n_b))
+        return DFKV_ERR_ALIAS;
+    AcceptArgs a{target, t_stride_req, t_stride_tok, draft, d_stride_req, d_stride_tok, n_reqs, width, n_acc_out,
+                 accepted_out};
+    return hip_status(launch_strict_accept(a, (hipStream_t)stream));
+}
+
 dfkv_status dfkv_join(dfkv_stream_t main, void *join) {
     if (!join) return DFKV_ERR_NULL;
     return hip_status(hipStreamWaitEvent((hipStream_t)main, (hipEvent_t)join, 0));

@@ -108,6 +108,17 @@ struct FinalizeParams {
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s);
 hipError_t launch_advance(const FinalizeParams &p, hipStream_t s);
 
+// Strict acceptance of a uniform-width draft (k_misc.hip)
+struct AcceptArgs {
+    const int32_t *target;
+    int64_t t_sr, t_st;
+    const int32_t *draft;
+    int64_t d_sr, d_st;
+    int32_t B, W;
+    int32_t *n_acc, *acc;
+};
+hipError_t launch_strict_accept(const AcceptArgs &a, hipStream_t s);
+
 // Draft-KV block-table decode (k_misc.hip)
 struct BtDecodeArgs {
     const int32_t *off;

@@ -202,3 +202,39 @@ hipError_t launch_bt_decode(const BtDecodeArgs &a, hipStream_t s) {
 }
 
 }  // namespace dfkv
+
+namespace dfkv {
+
+// ---------------------------------------------------------------------------
+// Strict acceptance of a uniform-width draft (the downstream commit quoted on
+// the TensorRT-LLM PR #20550 page): n_acc = 1 + the draft's prefix that equals
+// the target's tokens; the accepted tokens are the target's.  One wave per
+// request: lane i compares position i (i < K), the first mismatch is the
+// lowest lane with a mismatch (a ballot), and lanes copy the target's tokens.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_strict_accept(const AcceptArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= a.B) return;
+    const int K = a.W - 1;
+    int first = K;                        // first mismatching position, K when the draft matches fully
+    for (int i0 = 0; i0 < K; i0 += 64) {
+        const int i = i0 + lane;
+        const bool miss = i < K && a.draft[(int64_t)r * a.d_sr + (int64_t)i * a.d_st] !=
+                                       a.target[(int64_t)r * a.t_sr + (int64_t)i * a.t_st];
+        const unsigned long long m = __ballot(miss);
+        if (m) {
+            first = i0 + __ffsll((long long)m) - 1;
+            break;
+        }
+    }
+    if (lane == 0) a.n_acc[r] = 1 + first;
+    for (int i = lane; i < a.W; i += 64) a.acc[(int64_t)r * a.W + i] = a.target[(int64_t)r * a.t_sr + (int64_t)i * a.t_st];
+}
+
+hipError_t launch_strict_accept(const AcceptArgs &a, hipStream_t s) {
+    if (a.B <= 0) return hipSuccess;
+    return launch1(k_strict_accept, dim3((unsigned)((a.B + 3) / 4)), dim3(256), s, a);
+}
+
+}  // namespace dfkv

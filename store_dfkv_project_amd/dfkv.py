@@ -34,7 +34,8 @@ DFKV_FUSE_NORM_ROPE = 1
 
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
-            "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join", "dfkv_block_table_decode")
+            "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join", "dfkv_block_table_decode",
+            "dfkv_strict_accept")
 
 
 class dfkv_geom(C.Structure):
@@ -116,6 +117,7 @@ def _load() -> C.CDLL:
         "dfkv_project_fork": ([gp, wp, P, I64, I32, P, P, I32, P, U32, P, SZ, P, P, P, P], C.c_int),
         "dfkv_join": ([P, P], C.c_int),
         "dfkv_block_table_decode": ([P, I64, I64, I32, I32, P, I32, I32, P, P, I64, P], C.c_int),
+        "dfkv_strict_accept": ([P, I64, I64, P, I64, I64, I32, I32, P, P, P], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -263,6 +265,13 @@ def dfkv_block_table_decode(offsets, off_stride_req, off_stride_blk, n_reqs, max
                                         int(max_blocks), _ptr(n_tokens), int(page_size), int(divisor),
                                         _ptr(page_count_out), _ptr(table_out), int(table_row_stride),
                                         _stream(stream)), "dfkv_block_table_decode")
+
+
+def dfkv_strict_accept(target, t_stride_req, t_stride_tok, draft, d_stride_req, d_stride_tok, n_reqs, width,
+                       n_acc_out, accepted_out, stream=None) -> None:
+    _check(_lib.dfkv_strict_accept(_ptr(target), int(t_stride_req), int(t_stride_tok), _ptr(draft),
+                                   int(d_stride_req), int(d_stride_tok), int(n_reqs), int(width), _ptr(n_acc_out),
+                                   _ptr(accepted_out), _stream(stream)), "dfkv_strict_accept")
 
 
 def dfkv_join(main, join) -> None:

@@ -271,6 +271,19 @@ def test_block_table_decode_validation():
     assert status_of(f, **dict(base, n_reqs=0, offsets=None, n_tokens=None)) == dfkv.DFKV_OK
 
 
+def test_strict_accept_validation():
+    f = dfkv.dfkv_strict_accept
+    base = dict(target=addr(1), t_stride_req=4, t_stride_tok=1, draft=addr(2), d_stride_req=3, d_stride_tok=1,
+                n_reqs=8, width=4, n_acc_out=addr(3), accepted_out=addr(4), stream=0)
+    assert status_of(f, **dict(base, width=0)) == dfkv.DFKV_ERR_SHAPE
+    assert status_of(f, **dict(base, n_reqs=-1)) == dfkv.DFKV_ERR_SHAPE
+    assert status_of(f, **dict(base, draft=None)) == dfkv.DFKV_ERR_NULL
+    assert status_of(f, **dict(base, t_stride_tok=-1)) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(f, **dict(base, accepted_out=addr(1) + 32)) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(f, **dict(base, n_acc_out=addr(2) + 8)) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(f, **dict(base, n_reqs=0, target=None)) == dfkv.DFKV_OK
+
+
 def test_rope_cache_validation():
     r = dfkv.make_rope(1e6, 64)
     assert status_of(dfkv.dfkv_rope_cache_build, dfkv.make_rope(1e6, 63), addr(7), 10, stream=0) == \
