@@ -77,10 +77,11 @@ class Oracle:
         L.dfkv_oracle_block_placement.argtypes = [_I, _I, _I, _P, _P, _P, _P, _I64, _I, _I, _P]
         L.dfkv_oracle_block_table_decode.argtypes = [_I, _I, _P, _I64, _I64, _P, _I, _I, _P, _P, _I64]
         L.dfkv_oracle_strict_accept.argtypes = [_I, _I, _P, _I64, _I64, _P, _I64, _I64, _P, _P]
+        L.dfkv_oracle_row_slots.argtypes = [_I, _P, _P, _I, _P, _P, _I64, _I, _I, _I, _P, _P]
         for fn in ("dfkv_oracle_linear", "dfkv_oracle_rmsnorm", "dfkv_oracle_inv_freq", "dfkv_oracle_rope_cache",
                    "dfkv_oracle_rope_neox", "dfkv_oracle_norm_rope", "dfkv_oracle_project",
                    "dfkv_oracle_bookkeeping", "dfkv_oracle_store", "dfkv_oracle_block_placement",
-                   "dfkv_oracle_block_table_decode", "dfkv_oracle_strict_accept"):
+                   "dfkv_oracle_block_table_decode", "dfkv_oracle_strict_accept", "dfkv_oracle_row_slots"):
             getattr(L, fn).restype = None
         self.lib = L
 
@@ -247,6 +248,21 @@ class Oracle:
         self.lib.dfkv_oracle_strict_accept(n_reqs, width, _ptr(t), t_sr, t_st, _ptr(d), d_sr, d_st, _ptr(n_acc),
                                            _ptr(acc))
         return n_acc, acc
+
+    def row_slots(self, geom, row_req, row_pos, n_reqs: int, alloc_limit, block_table, num_pages: int,
+                  bt_stride: Optional[int] = None):
+        """Destinations of prefill-shaped (ragged) rows: row n of request row_req[n] at position row_pos[n]
+        (the single-latent context scatter of the PR #20550 page at any row count).  Returns (slot, write_mask)."""
+        rq = np.ascontiguousarray(row_req, dtype=np.int32)
+        rp = np.ascontiguousarray(row_pos, dtype=np.int32)
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        bt_cols = bt.shape[1] if bt.ndim == 2 else int(bt.size // max(n_reqs, 1))
+        bt_stride = bt_cols if bt_stride is None else bt_stride
+        n = rq.size
+        slot, wm = np.empty(n, np.int64), np.empty(n, np.uint8)
+        self.lib.dfkv_oracle_row_slots(n, _ptr(rq), _ptr(rp), n_reqs, _ptr(np.ascontiguousarray(alloc_limit, np.int32)),
+                                       _ptr(bt), bt_stride, bt_cols, geom.page_size, num_pages, _ptr(slot), _ptr(wm))
+        return slot, wm
 
     def store(self, geom, kv: np.ndarray, slot: np.ndarray, write_mask: np.ndarray, pools_k: Sequence[np.ndarray],
               pools_v: Optional[Sequence[np.ndarray]], s_page: int, s_slot: int, s_head: int) -> None:

@@ -497,6 +497,38 @@ EXPORT void dfkv_oracle_strict_accept(int B, int W, const int32_t *target, int64
 }
 
 /* ------------------------------------------------------------------------ */
+/* Destinations of prefill-shaped (ragged) context rows: the single-latent   */
+/* context scatter the PR #20550 page lists among its fused kernels, at any  */
+/* per-request row count.  Row n belongs to request r = row_req[n] at        */
+/* position pos = row_pos[n]:                                                */
+/*   w = 0 <= r < B && 0 <= pos < lim[r] && pos/pg < bt_cols                 */
+/*       && 0 <= page < num_pages, page = block_table[r][pos/pg]             */
+/*   slot = w ? page*pg + pos%pg : -1                                        */
+/* (the rows are then stored by dfkv_oracle_store).                          */
+/* ------------------------------------------------------------------------ */
+
+EXPORT void dfkv_oracle_row_slots(int n_rows, const int32_t *row_req, const int32_t *row_pos, int B,
+                                  const int32_t *alloc_limit, const int32_t *bt, int64_t bt_stride, int bt_cols,
+                                  int pg, int num_pages, int64_t *slot_out, uint8_t *write_mask_out)
+{
+    for (int n = 0; n < n_rows; ++n) {
+        int32_t r = row_req[n];
+        int64_t pos = row_pos[n], slot = -1;
+        if (r >= 0 && r < B && pos >= 0 && pos < alloc_limit[r] && pos / pg < bt_cols) {
+            int32_t page = bt[(int64_t)r * bt_stride + pos / pg];
+#if DFKV_ORACLE_MUTANT == 11 /* planted: the page bound off by one */
+            if (page >= 0 && page <= num_pages)
+#else
+            if (page >= 0 && page < num_pages)
+#endif
+                slot = (int64_t)page * pg + pos % pg;
+        }
+        slot_out[n] = slot;
+        write_mask_out[n] = (uint8_t)(slot >= 0);
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Paged store: every written row goes into every layer's pool.              */
 /* GQA: layer l's K pool gets kv[row][l][0][h][:] at                         */
 /*      page*s_page + off*s_slot + h*s_head, its V pool kv[row][l][1][h][:]. */

@@ -670,6 +670,61 @@ def pin_strict_accept_feeds_bookkeeping(o):
 
 
 # ---------------------------------------------------------------------------
+# prefill-shaped (ragged) rows: destinations
+# ---------------------------------------------------------------------------
+
+def pin_row_slots_position_first(o):
+    """Walk every table entry of every request and find the rows that must land in each of its slots."""
+    geom = Geometry(kind=GQA, n_tgt=1, tgt_hidden=8, hidden=8, n_layers=1, n_kv_heads=1, head_dim=8, latent_dim=0,
+                    rope_dim=8, eps=1e-6, page_size=4, width=1, block_size=1)
+    rng = np.random.default_rng(69)
+    for _ in range(200):
+        B, cols, P = int(rng.integers(1, 5)), int(rng.integers(1, 5)), 24
+        tbl = rng.permutation(P)[:B * cols].reshape(B, cols).astype(np.int32)
+        tbl[rng.random((B, cols)) < 0.2] = -1
+        if rng.random() < 0.2:
+            tbl[0, 0] = P                                  # one past the last page
+        lim = rng.integers(0, cols * 4 + 3, size=B).astype(np.int32)
+        n = int(rng.integers(1, 30))
+        rq = rng.integers(-1, B + 1, size=n).astype(np.int32)
+        rp = rng.integers(-2, cols * 4 + 4, size=n).astype(np.int32)
+        slot, wm = o.row_slots(geom, rq, rp, B, lim, tbl, P)
+        want = np.full(n, -1, np.int64)
+        for r in range(B):
+            for q in range(cols):
+                page = int(tbl[r, q])
+                if not 0 <= page < P:
+                    continue
+                for off in range(4):
+                    p = q * 4 + off
+                    if p >= lim[r]:
+                        continue
+                    for row in range(n):
+                        if rq[row] == r and rp[row] == p:
+                            want[row] = page * 4 + off
+        assert np.array_equal(slot, want), (slot, want)
+        assert np.array_equal(wm, (want >= 0).astype(np.uint8))
+
+
+def pin_row_slots_match_uniform_bookkeeping(o):
+    """A uniform batch with every row accepted, written row by row, gets the bookkeeping's slots."""
+    geom = Geometry(kind=GQA, n_tgt=1, tgt_hidden=8, hidden=8, n_layers=1, n_kv_heads=1, head_dim=8, latent_dim=0,
+                    rope_dim=8, eps=1e-6, page_size=4, width=3, block_size=2)
+    rng = np.random.default_rng(70)
+    B, W, P = 8, 3, 64
+    tbl = rng.permutation(P)[:B * 5].reshape(B, 5).astype(np.int32)
+    tbl[rng.random((B, 5)) < 0.2] = -1
+    ctx = rng.integers(0, 18, size=B).astype(np.int32)
+    lim = (ctx + rng.integers(0, 5, size=B)).astype(np.int32)
+    acc = np.zeros((B, W), np.int32)
+    bk = o.bookkeeping(geom, B, ctx, np.full(B, W, np.int32), lim, np.zeros(B, np.uint8), None, tbl, acc, W, 1, 1, P)
+    rq = np.repeat(np.arange(B, dtype=np.int32), W)
+    rp = (np.repeat(ctx, W) + np.tile(np.arange(W, dtype=np.int32), B)).astype(np.int32)
+    slot, wm = o.row_slots(geom, rq, rp, B, lim, tbl, P)
+    assert np.array_equal(slot, bk["slot"]) and np.array_equal(wm, bk["write_mask"])
+
+
+# ---------------------------------------------------------------------------
 # paged store
 # ---------------------------------------------------------------------------
 
