@@ -27,6 +27,7 @@ Prints ONE JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -238,6 +239,50 @@ def measure_accept(stream, timed, B: int = 256, W: int = 16) -> dict:
     return {"requests": B, "width": W, "us_per_launch": round(us, 2)}
 
 
+def measure_store_rows(wl, stream, timed, N: int = 4096) -> dict:
+    """dfkv_paged_store_rows for a prefill of N rows of one request at the workload's geometry (rows at
+    positions 0..N-1 over shuffled pages), 10 launches per captured graph; HBM bytes = the rows read once
+    and written once."""
+    import numpy as np
+    import torch
+    from store_dfkv_project_amd import dfkv
+    from store_dfkv_project_amd.step import geom_struct
+    g = dataclasses.replace(wl.geom, width=1)
+    pg, L, O = g.page_size, g.n_layers, g.out_dim
+    pages = (N + pg - 1) // pg
+    P = pages + 8
+    rng = np.random.default_rng(9)
+    gs = geom_struct(g)
+    kv = torch.randint(-32768, 32768, (N, O), dtype=torch.int16, device="cuda")
+    rq = torch.zeros(N, dtype=torch.int32, device="cuda")
+    rp = torch.arange(N, dtype=torch.int32, device="cuda")
+    lim = torch.tensor([N], dtype=torch.int32, device="cuda")
+    bt = torch.from_numpy(rng.permutation(P)[:pages].astype(np.int32).reshape(1, pages)).cuda()
+    if g.kind == 0:
+        slot_elems = g.n_kv_heads * g.head_dim
+        pk = torch.zeros((L, P, pg, slot_elems), dtype=torch.int16, device="cuda")
+        pv = torch.zeros_like(pk)
+        pool = dfkv.make_pool([pk[l] for l in range(L)], [pv[l] for l in range(L)], pg * slot_elems, slot_elems,
+                              g.head_dim, P)
+    else:
+        slot_elems = g.latent_dim + g.rope_dim
+        pk = torch.zeros((L, P, pg, slot_elems), dtype=torch.int16, device="cuda")
+        pool = dfkv.make_pool([pk[l] for l in range(L)], None, pg * slot_elems, slot_elems, 0, P)
+    slot = torch.zeros(N, dtype=torch.int64, device="cuda")
+    wm = torch.zeros(N, dtype=torch.uint8, device="cuda")
+    per = 10
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr, stream=stream):
+        for _ in range(per):
+            dfkv.dfkv_paged_store_rows(gs, kv, N, rq, rp, 1, lim, bt, pages, pages, pool, slot, wm, stream)
+    torch.cuda.synchronize()
+    us = float(timed([gr], 10, 2, per).mean())
+    nbytes = 2 * N * O * 2 + N * 9
+    return {"rows": N, "layers": L, "row_bytes": O * 2, "us_per_launch": round(us, 2), "bytes_per_launch": nbytes,
+            "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,6 +428,7 @@ def main() -> int:
                                                            args.window_us)
     bt_decode = measure_bt_decode(stream, timed)
     accept = measure_accept(stream, timed)
+    rows_store = measure_store_rows(wl, stream, timed)
 
     out = {
         "metric": METRIC,
@@ -414,6 +460,7 @@ def main() -> int:
         out["overlap"] = overlap
     out["block_table_decode"] = bt_decode
     out["strict_accept"] = accept
+    out["paged_store_rows"] = rows_store
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -312,6 +312,27 @@ dfkv_status dfkv_paged_store(const dfkv_geom *g, const void *kv, const dfkv_requ
                              const dfkv_pool *pool, int64_t *slot_out, uint8_t *write_mask_out,
                              dfkv_stream_t stream);
 
+/* Row-wise paged store of prefill-shaped (ragged) context ([P20550]: the
+ * single-latent context scatter, here at any per-request row count): row n of
+ * kv ([n_rows][O] bf16, as dfkv_project writes it) belongs to request
+ * row_req[n] at position row_pos[n].  It is written into every layer's pool
+ * (same layout rules as dfkv_paged_store) when 0 <= r < n_reqs,
+ * 0 <= pos < alloc_limit[r], pos/page_size < bt_cols and 0 <= page < num_pages
+ * with page = block_table[r*bt_row_stride + pos/page_size]; slot_out[n] =
+ * page*page_size + pos%page_size or -1, write_mask_out[n] = 1 iff written.
+ * Every other pool byte is unchanged.  The rows' projection is dfkv_project
+ * with geom.width = 1 and ctx_len_in = row_pos (each row its own RoPE
+ * position).  A dense per-slot buffer [max_batch][L][T][nkv][hd] is this pool
+ * with page_size = T, one page per request (its batch slot) and stride_page =
+ * L*T*nkv*hd, k[l] = buffer + l*T*nkv*hd.
+ * Errors: NULL, SHAPE, LAYOUT (pool, table stride), ALIAS (outputs over inputs
+ * or pools, kv over a pool), HIP. */
+dfkv_status dfkv_paged_store_rows(const dfkv_geom *g, const void *kv, int32_t n_rows, const int32_t *row_req,
+                                  const int32_t *row_pos, int32_t n_reqs, const int32_t *alloc_limit,
+                                  const int32_t *block_table, int64_t bt_row_stride, int32_t bt_cols,
+                                  const dfkv_pool *pool, int64_t *slot_out, uint8_t *write_mask_out,
+                                  dfkv_stream_t stream);
+
 /* Per-request advance ([P20550] TLLM_DFLASH_FUSED_PROLOGUE: bonus token, query
  * and context positions, embedding ids, ctx_len advance with the clamp and the
  * dummy-slot reset, advertised context length; downstream commit: seq_lens;

@@ -272,9 +272,8 @@ dfkv_status check_pool(const dfkv_geom *g, const dfkv_pool *pool) {
 
 size_t pool_bytes(const dfkv_geom *g, const dfkv_pool *pool) { return (size_t)pool->num_pages * pool->stride_page * 2; }
 
-dfkv_status check_store_outputs(const dfkv_geom *g, const dfkv_requests *r, const dfkv_pool *pool, const void *kv,
-                                const int64_t *slot, const uint8_t *wmask) {
-    const int64_t N = (int64_t)r->n_reqs * g->width;
+dfkv_status check_store_outputs_n(const dfkv_geom *g, int64_t N, const dfkv_pool *pool, const void *kv,
+                                  const int64_t *slot, const uint8_t *wmask) {
     if (N == 0) return DFKV_OK;
     if (!kv || !slot || !wmask) return DFKV_ERR_NULL;
     if (!al16(kv) || ((uintptr_t)slot & 7u)) return DFKV_ERR_LAYOUT;
@@ -294,6 +293,11 @@ dfkv_status check_store_outputs(const dfkv_geom *g, const dfkv_requests *r, cons
         if (g->kind == DFKV_GQA && overlap(kv, kvb, pool->v[l], pb)) return DFKV_ERR_ALIAS;
     }
     return DFKV_OK;
+}
+
+dfkv_status check_store_outputs(const dfkv_geom *g, const dfkv_requests *r, const dfkv_pool *pool, const void *kv,
+                                const int64_t *slot, const uint8_t *wmask) {
+    return check_store_outputs_n(g, (int64_t)r->n_reqs * g->width, pool, kv, slot, wmask);
 }
 
 dfkv_status check_adv_outputs(const dfkv_geom *g, const dfkv_requests *r, const dfkv_outputs *o) {
@@ -746,6 +750,42 @@ dfkv_status dfkv_paged_store(const dfkv_geom *g, const void *kv, const dfkv_requ
     p.src = (const uint16_t *)kv;
     p.store = 1;
     return hip_status(launch_finalize(p, (hipStream_t)stream));
+}
+
+dfkv_status dfkv_paged_store_rows(const dfkv_geom *g, const void *kv, int32_t n_rows, const int32_t *row_req,
+                                  const int32_t *row_pos, int32_t n_reqs, const int32_t *alloc_limit,
+                                  const int32_t *block_table, int64_t bt_row_stride, int32_t bt_cols,
+                                  const dfkv_pool *pool, int64_t *slot_out, uint8_t *write_mask_out,
+                                  dfkv_stream_t stream) {
+    dfkv_status st = check_geom(g);
+    if (st != DFKV_OK) return st;
+    if (n_rows < 0 || n_reqs < 0) return DFKV_ERR_SHAPE;
+    if (n_rows == 0) return DFKV_OK;
+    if (!row_req || !row_pos || (n_reqs > 0 && (!alloc_limit || !block_table))) return DFKV_ERR_NULL;
+    if (n_reqs > 0 && (bt_cols <= 0 || bt_row_stride < bt_cols)) return DFKV_ERR_LAYOUT;
+    if ((st = check_pool(g, pool)) != DFKV_OK) return st;
+    if ((st = check_store_outputs_n(g, n_rows, pool, kv, slot_out, write_mask_out)) != DFKV_OK) return st;
+    const size_t nb = (size_t)n_rows * 4, rb = (size_t)n_reqs * 4;
+    const size_t bb = n_reqs > 0 ? extent2(bt_row_stride, n_reqs, 1, bt_cols) : 0;
+    const void *ins[4] = {row_req, row_pos, alloc_limit, block_table};
+    const size_t ib[4] = {nb, nb, rb, bb};
+    for (int j = 0; j < 4; ++j)
+        if (overlap(slot_out, (size_t)n_rows * 8, ins[j], ib[j]) || overlap(write_mask_out, (size_t)n_rows, ins[j], ib[j]))
+            return DFKV_ERR_ALIAS;
+    FinalizeParams p = fin_params(g, nullptr, pool, nullptr, 0);
+    p.M = n_rows;
+    p.B = n_reqs;
+    p.limit = alloc_limit;
+    p.bt = block_table;
+    p.bt_stride = bt_row_stride;
+    p.bt_cols = bt_cols;
+    p.row_req = row_req;
+    p.row_pos = row_pos;
+    p.slot = slot_out;
+    p.wmask = write_mask_out;
+    p.src = (const uint16_t *)kv;
+    p.store = 1;
+    return hip_status(launch_store_rows(p, (hipStream_t)stream));
 }
 
 dfkv_status dfkv_advance(const dfkv_geom *g, const dfkv_requests *req, const dfkv_outputs *out, dfkv_stream_t stream) {

@@ -104,9 +104,11 @@ struct FinalizeParams {
     uint8_t *wmask;
     int32_t *c_pos, *bonus, *emb, *q_pos, *ctx_out, *seq_len;
     int64_t *block_slot;   // [B][bs_blk] or null: placement of the next draft block
+    const int32_t *row_req, *row_pos;   // row-wise store: each row's request and position
 };
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s);
 hipError_t launch_advance(const FinalizeParams &p, hipStream_t s);
+hipError_t launch_store_rows(const FinalizeParams &p, hipStream_t s);   // p.M rows x p.L layers
 
 // Strict acceptance of a uniform-width draft (k_misc.hip)
 struct AcceptArgs {

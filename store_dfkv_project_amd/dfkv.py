@@ -35,7 +35,7 @@ DFKV_FUSE_NORM_ROPE = 1
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
             "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join", "dfkv_block_table_decode",
-            "dfkv_strict_accept")
+            "dfkv_strict_accept", "dfkv_paged_store_rows")
 
 
 class dfkv_geom(C.Structure):
@@ -118,6 +118,7 @@ def _load() -> C.CDLL:
         "dfkv_join": ([P, P], C.c_int),
         "dfkv_block_table_decode": ([P, I64, I64, I32, I32, P, I32, I32, P, P, I64, P], C.c_int),
         "dfkv_strict_accept": ([P, I64, I64, P, I64, I64, I32, I32, P, P, P], C.c_int),
+        "dfkv_paged_store_rows": ([gp, P, I32, P, P, I32, P, P, I64, I32, pp, P, P, P], C.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -272,6 +273,14 @@ def dfkv_strict_accept(target, t_stride_req, t_stride_tok, draft, d_stride_req, 
     _check(_lib.dfkv_strict_accept(_ptr(target), int(t_stride_req), int(t_stride_tok), _ptr(draft),
                                    int(d_stride_req), int(d_stride_tok), int(n_reqs), int(width), _ptr(n_acc_out),
                                    _ptr(accepted_out), _stream(stream)), "dfkv_strict_accept")
+
+
+def dfkv_paged_store_rows(geom, kv, n_rows, row_req, row_pos, n_reqs, alloc_limit, block_table, bt_row_stride,
+                          bt_cols, pool, slot_out, write_mask_out, stream=None) -> None:
+    _check(_lib.dfkv_paged_store_rows(_ref(geom), _ptr(kv), int(n_rows), _ptr(row_req), _ptr(row_pos), int(n_reqs),
+                                      _ptr(alloc_limit), _ptr(block_table), int(bt_row_stride), int(bt_cols),
+                                      _ref(pool), _ptr(slot_out), _ptr(write_mask_out), _stream(stream)),
+           "dfkv_paged_store_rows")
 
 
 def dfkv_join(main, join) -> None:

@@ -284,6 +284,20 @@ def test_strict_accept_validation():
     assert status_of(f, **dict(base, n_reqs=0, target=None)) == dfkv.DFKV_OK
 
 
+def test_paged_store_rows_validation():
+    f = dfkv.dfkv_paged_store_rows
+    base = dict(geom=geom(), kv=addr(60), n_rows=10, row_req=addr(61), row_pos=addr(62), n_reqs=2,
+                alloc_limit=addr(63), block_table=addr(64), bt_row_stride=8, bt_cols=8, pool=pool(),
+                slot_out=addr(50), write_mask_out=addr(51), stream=0)
+    assert status_of(f, **dict(base, n_rows=-1)) == dfkv.DFKV_ERR_SHAPE
+    assert status_of(f, **dict(base, row_pos=None)) == dfkv.DFKV_ERR_NULL
+    assert status_of(f, **dict(base, bt_row_stride=4)) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(f, **dict(base, slot_out=addr(61) + 8)) == dfkv.DFKV_ERR_ALIAS     # over row_req
+    assert status_of(f, **dict(base, kv=addr(30))) == dfkv.DFKV_ERR_ALIAS               # kv over a pool
+    assert status_of(f, **dict(base, pool=pool(stride_slot=3))) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(f, **dict(base, n_rows=0, kv=None)) == dfkv.DFKV_OK
+
+
 def test_rope_cache_validation():
     r = dfkv.make_rope(1e6, 64)
     assert status_of(dfkv.dfkv_rope_cache_build, dfkv.make_rope(1e6, 63), addr(7), 10, stream=0) == \
