@@ -15,8 +15,8 @@
 //    weights, one eps) and commit "match RoPE between context and query for
 //    YaRN" (context K rotated from the one cos/sin cache).
 //
-// One workgroup per (token row, drafter layer).  The row's stacked projection
-// for that layer is read either as fp32 split-K partial sums (summed in split
+// One workgroup per token row, looping over the drafter layers.  The row's
+// stacked projection is read either as fp32 split-K partial sums (summed in split
 // order, then rounded to bf16 -- the K/V GEMM output) or as bf16 rows.  With
 // `norm`, each K head (GQA) or the latent (MLA) is RMS-normalised by one wave
 // (wave-level reduction) and rotated (NeoX pairs held by one lane), the rope
@@ -53,33 +53,36 @@ __device__ __forceinline__ u32x4 load_y8(const FinalizeParams &p, int row, int64
 
 constexpr int kFinThreads = 512;  // 8 waves: one K head per wave for up to 8 KV heads
 
+// One workgroup per token row, every drafter layer: the row's destination (request fields, then the
+// block-table entry) is looked up once, its loads issued before the first layer's.
 __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p) {
     const int L = p.L;
-    const int row = blockIdx.x / L, l = blockIdx.x - (blockIdx.x / L) * L;
+    const int row = blockIdx.x;
     const int r = row / p.W, i = row - (row / p.W) * p.W;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     constexpr int NW = kFinThreads / 64;
 
-    if (p.advance && i == 0 && l == 0) request_advance(p, r);
-    const int64_t lay = (int64_t)l * p.per_layer;
-    uint16_t *const out = p.kv_out ? p.kv_out + (int64_t)row * p.O + lay : nullptr;
+    if (p.advance && i == 0) request_advance(p, r);
+    int64_t slot = -1;
+    const bool w = p.store && row_destination(p, r, i, row, slot);
+    if (p.store && tid == 0) {
+        p.slot[row] = slot;
+        p.wmask[row] = w ? 1 : 0;
+    }
+    const int64_t dst0 = w ? slot_offset(p, slot) : 0;
+    uint16_t *const out_row = p.kv_out ? p.kv_out + (int64_t)row * p.O : nullptr;
 
     if (!p.norm) {
         // final K/V rows in hand (paged store of a finished projection, or plain rounding of the
-        // partial sums): 16-byte chunks straight through, pool writes only for written rows
-        int64_t slot = -1;
-        const bool w = p.store && row_destination(p, r, i, row, slot);
-        if (p.store && l == 0 && tid == 0) {
-            p.slot[row] = slot;
-            p.wmask[row] = w ? 1 : 0;
-        }
-        if (!out && !w) return;
-        const int64_t dst0 = w ? slot_offset(p, slot) : 0;
+        // partial sums): 16-byte chunks of every layer straight through, pool writes only for
+        // written rows
+        if (!out_row && !w) return;
         const int nch = p.per_layer >> 3;
-        for (int c = tid; c < nch; c += kFinThreads) {
-            const int e = c << 3;
+        for (int c = tid; c < L * nch; c += kFinThreads) {
+            const int l = c / nch, e = (c - l * nch) << 3;
+            const int64_t lay = (int64_t)l * p.per_layer;
             const u32x4 v = load_y8(p, row, lay + e);
-            if (out) *(u32x4 *)(out + e) = v;
+            if (out_row) *(u32x4 *)(out_row + lay + e) = v;
             if (w) {
                 if (p.kind == DFKV_GQA) {
                     const int kvh = p.nkv * p.hd;
@@ -98,13 +101,22 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
     if (p.kind == DFKV_GQA) {
         const int hd = p.hd, nkv = p.nkv, half = hd >> 1;
         const int kvh = nkv * hd;
-        // 1. independent loads first: this thread's V chunk and this wave's first K head
         const int vch = kvh >> 3;
-        u32x4 vv = u32x4{0u, 0u, 0u, 0u};
-        if (tid < vch) vv = load_y8(p, row, lay + kvh + (tid << 3));
-        float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
-        int h = wave;
-        if (h < nkv) {
+        const float *cs = rope_row(p.nr, row);
+        // V of every layer straight through (16-byte chunks)
+        for (int c = tid; c < L * vch; c += kFinThreads) {
+            const int l = c / vch, cc = c - l * vch;
+            const int64_t lay = (int64_t)l * p.per_layer;
+            const u32x4 v = load_y8(p, row, lay + kvh + (cc << 3));
+            const int hh = cc / (hd >> 3), e = (cc - hh * (hd >> 3)) << 3;
+            if (out_row) *(u32x4 *)(out_row + lay + kvh + (cc << 3)) = v;
+            if (w) *(u32x4 *)(p.pv[l] + dst0 + (int64_t)hh * p.sh + e) = v;
+        }
+        // K heads of every layer: k_norm then RoPE, one wave per (layer, head)
+        for (int item = wave; item < L * nkv; item += NW) {
+            const int l = item / nkv, h = item - l * nkv;
+            const int64_t lay = (int64_t)l * p.per_layer;
+            float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
                 const int j = lane + q2 * 64;
@@ -113,46 +125,15 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
                     b[q2] = load_y(p, row, lay + h * hd + j + half);
                 }
             }
-        }
-        // 2. the row's destination
-        int64_t slot = -1;
-        const bool w = p.store && row_destination(p, r, i, row, slot);
-        if (p.store && l == 0 && tid == 0) {
-            p.slot[row] = slot;
-            p.wmask[row] = w ? 1 : 0;
-        }
-        const int64_t dst0 = w ? slot_offset(p, slot) : 0;
-        // 3. V straight through
-        for (int c = tid; c < vch; c += kFinThreads) {
-            const u32x4 v = c == tid ? vv : load_y8(p, row, lay + kvh + (c << 3));
-            const int hh = c / (hd >> 3), e = (c - hh * (hd >> 3)) << 3;
-            if (out) *(u32x4 *)(out + kvh + (c << 3)) = v;
-            if (w) *(u32x4 *)(p.pv[l] + dst0 + (int64_t)hh * p.sh + e) = v;
-        }
-        // 4. K heads: k_norm then RoPE, one wave per head
-        const float *cs = rope_row(p.nr, row);
-        const uint16_t *wk = p.nr.w_knorm + (int64_t)l * hd;
-        for (; h < nkv; h += NW) {
-            if (h != wave) {
-#pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) {
-                    const int j = lane + q2 * 64;
-                    a[q2] = b[q2] = 0.f;
-                    if (j < half) {
-                        a[q2] = load_y(p, row, lay + h * hd + j);
-                        b[q2] = load_y(p, row, lay + h * hd + j + half);
-                    }
-                }
-            }
             uint16_t ka[2], kb[2];
-            knorm_rope_head(a, b, hd, p.nr.eps, wk, cs, lane, ka, kb);
+            knorm_rope_head(a, b, hd, p.nr.eps, p.nr.w_knorm + (int64_t)l * hd, cs, lane, ka, kb);
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
                 const int j = lane + q2 * 64;
                 if (j < half) {
-                    if (out) {
-                        out[h * hd + j] = ka[q2];
-                        out[h * hd + j + half] = kb[q2];
+                    if (out_row) {
+                        out_row[lay + h * hd + j] = ka[q2];
+                        out_row[lay + h * hd + j + half] = kb[q2];
                     }
                     if (w) {
                         uint16_t *d = p.pk[l] + dst0 + (int64_t)h * p.sh;
@@ -163,50 +144,47 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
             }
         }
     } else {
-        // MLA: wave 0 normalises the latent and rotates the rope part
-        if (wave != 0) return;
+        // MLA: one wave per layer normalises the latent and rotates the rope part
         const int R = p.nr.latent, P = p.nr.rope_dim, half = P >> 1;
-        float v[16];
+        const float *cs = rope_row(p.nr, row);
+        for (int l = wave; l < L; l += NW) {
+            const int64_t lay = (int64_t)l * p.per_layer;
+            uint16_t *const out = out_row ? out_row + lay : nullptr;
+            float v[16];
 #pragma unroll
-        for (int q2 = 0; q2 < 16; ++q2) {
-            const int e = lane + q2 * 64;
-            v[q2] = e < R ? load_y(p, row, lay + e) : 0.f;
-        }
-        float ra = 0.f, rb = 0.f;
-        if (lane < half) {
-            ra = load_y(p, row, lay + R + lane);
-            rb = load_y(p, row, lay + R + lane + half);
-        }
-        int64_t slot = -1;
-        const bool w = p.store && row_destination(p, r, i, row, slot);
-        if (p.store && l == 0 && lane == 0) {
-            p.slot[row] = slot;
-            p.wmask[row] = w ? 1 : 0;
-        }
-        uint16_t *d = w ? p.pk[l] + slot_offset(p, slot) : nullptr;
-        const float rinv = latent_rinv(v, R, p.nr.eps);
-        const uint16_t *wk = p.nr.w_knorm + (int64_t)l * R;
+            for (int q2 = 0; q2 < 16; ++q2) {
+                const int e = lane + q2 * 64;
+                v[q2] = e < R ? load_y(p, row, lay + e) : 0.f;
+            }
+            float ra = 0.f, rb = 0.f;
+            if (lane < half) {
+                ra = load_y(p, row, lay + R + lane);
+                rb = load_y(p, row, lay + R + lane + half);
+            }
+            uint16_t *d = w ? p.pk[l] + dst0 : nullptr;
+            const float rinv = latent_rinv(v, R, p.nr.eps);
+            const uint16_t *wk = p.nr.w_knorm + (int64_t)l * R;
 #pragma unroll
-        for (int q2 = 0; q2 < 16; ++q2) {
-            const int e = lane + q2 * 64;
-            if (e < R) {
-                const uint16_t o = latent_elem(wk[e], v[q2], rinv);
-                if (out) out[e] = o;
-                if (d) d[e] = o;
+            for (int q2 = 0; q2 < 16; ++q2) {
+                const int e = lane + q2 * 64;
+                if (e < R) {
+                    const uint16_t o = latent_elem(wk[e], v[q2], rinv);
+                    if (out) out[e] = o;
+                    if (d) d[e] = o;
+                }
             }
-        }
-        if (lane < half) {
-            const float *cs = rope_row(p.nr, row);
-            const float c = cs[lane], sn = cs[half + lane];
-            uint16_t ka, kb;
-            rope_pair(ra, rb, c, sn, ka, kb);
-            if (out) {
-                out[R + lane] = ka;
-                out[R + lane + half] = kb;
-            }
-            if (d) {
-                d[R + lane] = ka;
-                d[R + lane + half] = kb;
+            if (lane < half) {
+                const float c = cs[lane], sn = cs[half + lane];
+                uint16_t ka, kb;
+                rope_pair(ra, rb, c, sn, ka, kb);
+                if (out) {
+                    out[R + lane] = ka;
+                    out[R + lane + half] = kb;
+                }
+                if (d) {
+                    d[R + lane] = ka;
+                    d[R + lane + half] = kb;
+                }
             }
         }
     }
@@ -262,7 +240,7 @@ hipError_t launch_store_rows(const FinalizeParams &p, hipStream_t s) {
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s) {
     const int64_t N = (int64_t)p.B * p.W;
     if (N == 0) return hipSuccess;
-    return launch1(k_finalize, dim3((unsigned)(N * p.L)), dim3(kFinThreads), s, p);
+    return launch1(k_finalize, dim3((unsigned)N), dim3(kFinThreads), s, p);
 }
 
 hipError_t launch_advance(const FinalizeParams &p, hipStream_t s) {
