@@ -108,7 +108,7 @@ struct FinalizeParams {
 };
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s);
 hipError_t launch_advance(const FinalizeParams &p, hipStream_t s);
-hipError_t launch_store_rows(const FinalizeParams &p, hipStream_t s);   // p.M rows x p.L layers
+hipError_t launch_store_rows(const FinalizeParams &p, hipStream_t s);   // p.M rows, every layer
 
 // Strict acceptance of a uniform-width draft (k_misc.hip)
 struct AcceptArgs {

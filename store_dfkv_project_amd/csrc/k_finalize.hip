@@ -196,11 +196,10 @@ __global__ __launch_bounds__(64) void k_advance(const FinalizeParams p) { reques
 // Row-wise paged store of prefill-shaped (ragged) rows (the single-latent context scatter the
 // TensorRT-LLM PR #20550 page lists, at any row count): row n of request row_req[n] at position
 // row_pos[n] is written when 0 <= r < B, 0 <= pos < limit[r], pos/pg < bt_cols and the page is in
-// [0, num_pages).  One workgroup per (row, layer); the layer's slice moves as 16-byte chunks.
+// [0, num_pages).  One workgroup per row; every layer's slice moves as 16-byte chunks.
 constexpr int kRowThreads = 256;
 __global__ __launch_bounds__(kRowThreads) void k_store_rows(const FinalizeParams p) {
-    const int L = p.L;
-    const int row = blockIdx.x / L, l = blockIdx.x - (blockIdx.x / L) * L;
+    const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int32_t r = p.row_req[row];
     const int64_t pos = p.row_pos[row];
@@ -210,16 +209,17 @@ __global__ __launch_bounds__(kRowThreads) void k_store_rows(const FinalizeParams
         const int32_t page = p.bt[(int64_t)r * p.bt_stride + pidx];
         if (page >= 0 && page < p.num_pages) slot = (int64_t)page * p.pg + (pos - pidx * p.pg);
     }
-    if (l == 0 && tid == 0) {
+    if (tid == 0) {
         p.slot[row] = slot;
         p.wmask[row] = slot >= 0 ? 1 : 0;
     }
     if (slot < 0) return;
-    const int64_t dst0 = slot_offset(p, slot), lay = (int64_t)l * p.per_layer;
-    const uint16_t *src = p.src + (int64_t)row * p.O + lay;
-    for (int c = tid; c < (p.per_layer >> 3); c += kRowThreads) {
-        const int e = c << 3;
-        const u32x4 v = *(const u32x4 *)(src + e);
+    const int64_t dst0 = slot_offset(p, slot);
+    const uint16_t *src = p.src + (int64_t)row * p.O;
+    const int nch = p.per_layer >> 3;
+    for (int c = tid; c < p.L * nch; c += kRowThreads) {
+        const int l = c / nch, e = (c - l * nch) << 3;
+        const u32x4 v = *(const u32x4 *)(src + (int64_t)l * p.per_layer + e);
         if (p.kind == DFKV_GQA) {
             const int kvh = p.nkv * p.hd;
             const bool is_v = e >= kvh;
@@ -234,7 +234,7 @@ __global__ __launch_bounds__(kRowThreads) void k_store_rows(const FinalizeParams
 
 hipError_t launch_store_rows(const FinalizeParams &p, hipStream_t s) {
     if (p.M <= 0) return hipSuccess;
-    return launch1(k_store_rows, dim3((unsigned)p.M * (unsigned)p.L), dim3(kRowThreads), s, p);
+    return launch1(k_store_rows, dim3((unsigned)p.M), dim3(kRowThreads), s, p);
 }
 
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s) {
