@@ -123,6 +123,7 @@ struct Plan {
     bool kvfin;  // k_kvgroups + k_kvfinal run the K/V stage
     int S_kv;
     int S_fc;    // large batch: k splits of the fc GEMM (partials summed by hidden_norm)
+    bool kv_w;   // large batch: the K/V GEMM is k_gemm_w (g packed in its token order)
     int ntg;     // k_kvfin: tiles per K/V group
     // bookkeeping area of the small-batch K/V kernels; f [M][H]; small batch: ss [H/16][M] and K/V
     // partials [S][M][O]; large batch: g [M][H] and, when the fc GEMM is split, its partials [S][M][H]
@@ -145,7 +146,8 @@ dfkv_status make_plan(const dfkv_geom *g, int32_t n_reqs, Plan *pl) {
     size_t off = 0;
     p.off_book = off; off = up256(off + kv_book_bytes(g->rope_dim));
     p.off_f = off; off = up256(off + Mp * H * 2);
-    p.off_g = off; off = up256(off + Mp * H * 2);
+    p.kv_w = !p.skinny && gemm_w_rows((int)O) != 0 && H % 64 == 0;
+    p.off_g = off; off = up256(off + (p.kv_w ? (Mp + 63) / 64 * 64 : Mp) * H * 2);
     p.kvfin = M >= 1 && M <= kKvMaxRows && (int64_t)n_reqs * g->block_size <= kKvMaxBlockPositions &&
               choose_kv_groups(g, M, &p.S_kv, &p.ntg);
     if (p.skinny) {
@@ -435,7 +437,8 @@ dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int
     if (stages_g(pl)) return DFKV_OK;
     uint16_t *gb = (uint16_t *)(wsb + pl.off_g);
     const float *part = !pl.skinny && pl.S_fc > 1 ? (const float *)(wsb + pl.off_part) : nullptr;
-    return hip_status(launch_hidden_norm(f, part, pl.S_fc, (const uint16_t *)w_hnorm, gb, (int)pl.M, (int)H, g->eps, s));
+    return hip_status(
+        launch_hidden_norm(f, part, pl.S_fc, (const uint16_t *)w_hnorm, gb, (int)pl.M, (int)H, g->eps, pl.kv_w, s));
 }
 
 dfkv_status run_kvfin(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx, const float *cs,
@@ -482,7 +485,7 @@ dfkv_status run_kv(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx
     const uint16_t *gb = (const uint16_t *)(wsb + pl.off_g);
     GemmParams t2{gb, H, (const uint16_t *)w->w_kv, (uint16_t *)kv_out, O, nullptr, (int32_t)pl.M, (int32_t)H,
                   (int32_t)O, 1};
-    if ((e = launch_gemm(t2, s)) != hipSuccess) return hip_status(e);
+    if ((e = pl.kv_w ? launch_gemm_w(t2, s) : launch_gemm(t2, s)) != hipSuccess) return hip_status(e);
     if (!fuse && !need_finalize) return DFKV_OK;
     fin.part = nullptr;
     fin.src = (const uint16_t *)kv_out;  // in place: each element is read and written by one thread

@@ -132,9 +132,10 @@ struct BtDecodeArgs {
 };
 hipError_t launch_bt_decode(const BtDecodeArgs &a, hipStream_t s);
 
-// part != null: f = bf16(sum of the S fp32 partials [S][n_rows][H]) is formed and written first
+// part != null: f = bf16(sum of the S fp32 partials [S][n_rows][H]) is formed and written first;
+// packed: g in k_gemm_w's token order (gemm_pack_index), ceil(n_rows / 64) * 64 rows, padding zero
 hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint16_t *w, uint16_t *g, int n_rows,
-                              int H, float eps, hipStream_t s);
+                              int H, float eps, bool packed, hipStream_t s);
 hipError_t launch_rope_cache(const dfkv_rope &r, float *cs, int cache_len, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
@@ -194,5 +195,18 @@ struct GemmParams {
 };
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s);
 int gemm_tiles(int M, int O);   // output tiles of launch_gemm (times S workgroups)
+// K/V GEMM with 160-feature tiles (k_gemm_w): S = 1, bf16 out; gemm_w_rows(O) is 160 when O divides by it
+hipError_t launch_gemm_w(const GemmParams &p, hipStream_t s);
+int gemm_w_rows(int O);
+// Token operand of k_gemm_w, packed in MFMA fragment order: element k of token n (K = 64 * iters)
+// sits at gemm_pack_index(n, k, iters) (in bf16 elements).  Token n belongs to block b = n / 64,
+// fragment j = (n / 32) % 2, lane row fr = n % 32; k to stage it = k / 64, where k % 64 = 32 fh +
+// 8 s + e (lane half fh, MFMA slice s, element e); the 64 lanes (fr + 32 fh) of one (b, it, s, j)
+// hold 1 KB in a row.  The buffer spans ceil(M / 64) * 64 tokens.
+__host__ __device__ inline int64_t gemm_pack_index(int64_t n, int64_t k, int64_t iters) {
+    const int64_t b = n >> 6, j = (n >> 5) & 1, fr = n & 31;
+    const int64_t it = k >> 6, r = k & 63, fh = r >> 5, s = (r >> 3) & 3, e = r & 7;
+    return ((((b * iters + it) * 4 + s) * 2 + j) * 64 + fr + 32 * fh) * 8 + e;
+}
 
 }  // namespace dfkv

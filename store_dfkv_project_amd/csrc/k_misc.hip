@@ -11,7 +11,9 @@ namespace dfkv {
 // workgroup per row (used by the large-batch path; the small-batch path folds
 // it into the stacked GEMM's operand load).  When the fc GEMM was split over
 // k, f is first formed here: f = bf16(sum over the S fp32 partials, in split
-// order), written out and then normalised.
+// order), written out and then normalised.  With `packed`, g is written in the
+// fragment order of k_gemm_w's token operand (gemm_pack_index; H divides by 64)
+// and the rows up to the next multiple of 64 are zero.
 // ---------------------------------------------------------------------------
 struct HiddenNormArgs {
     const uint16_t *w;
@@ -19,6 +21,7 @@ struct HiddenNormArgs {
     const float *part;   // [S][n_rows][H] fp32 partial sums of f, or null (f is given)
     int S, n_rows, H;
     float eps;
+    int packed;
 };
 
 __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
@@ -27,6 +30,15 @@ __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
     const int H = a.H;
     const float eps = a.eps;
     const int row = blockIdx.x;
+    // 16-byte chunk c (elements 8c .. 8c+7) of row `row` of g
+    auto gdst = [&](int c) -> uint16_t * {
+        return a.packed ? g + gemm_pack_index(row, (int64_t)c << 3, H >> 6) : g + (int64_t)row * H + (c << 3);
+    };
+    if (row >= a.n_rows) {
+        // padding rows of the packed layout
+        for (int c = threadIdx.x; c < (H >> 3); c += blockDim.x) *(u32x4 *)gdst(c) = u32x4{0u, 0u, 0u, 0u};
+        return;
+    }
     uint16_t *x = a.f + (int64_t)row * H;
     __shared__ float red[4];
     float ss = 0.f;
@@ -68,15 +80,17 @@ __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             o[q] = pack2(bf_lo(wv[q]) * (bf_lo(v[q]) * rinv), bf_hi(wv[q]) * (bf_hi(v[q]) * rinv));
-        *(u32x4 *)(g + (int64_t)row * H + (c << 3)) = o;
+        *(u32x4 *)gdst(c) = o;
     }
 }
 
 hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint16_t *w, uint16_t *g, int n_rows,
-                              int H, float eps, hipStream_t s) {
+                              int H, float eps, bool packed, hipStream_t s) {
     if (n_rows == 0) return hipSuccess;
-    if (H % 8 != 0 || (part && S < 1)) return hipErrorInvalidValue;
-    return launch1(k_hidden_norm, dim3(n_rows), dim3(256), s, HiddenNormArgs{w, f, g, part, S, n_rows, H, eps});
+    if (H % (packed ? 64 : 8) != 0 || (part && S < 1)) return hipErrorInvalidValue;
+    const int grid = packed ? (n_rows + 63) / 64 * 64 : n_rows;
+    return launch1(k_hidden_norm, dim3(grid), dim3(256), s,
+                   HiddenNormArgs{w, f, g, part, S, n_rows, H, eps, packed ? 1 : 0});
 }
 
 // ---------------------------------------------------------------------------

@@ -62,6 +62,12 @@ GQA_G64 = Geometry(kind=GQA, n_tgt=3, tgt_hidden=256, hidden=256, n_layers=2, n_
                    rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
 GQA_G256 = Geometry(kind=GQA, n_tgt=1, tgt_hidden=640, hidden=512, n_layers=1, n_kv_heads=3, head_dim=256,
                     latent_dim=0, rope_dim=256, eps=1e-6, page_size=16, width=3, block_size=4)
+# stacked K/V widths divisible by 160 (5 layers x 2 x nkv x 64): the large-batch K/V GEMM with
+# 160-feature tiles and the packed normalised hidden state
+GQA_W1 = Geometry(kind=GQA, n_tgt=2, tgt_hidden=256, hidden=256, n_layers=5, n_kv_heads=1, head_dim=64, latent_dim=0,
+                  rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
+GQA_W2 = Geometry(kind=GQA, n_tgt=1, tgt_hidden=384, hidden=384, n_layers=5, n_kv_heads=2, head_dim=64, latent_dim=0,
+                  rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
 MLA_G = Geometry(kind=MLA, n_tgt=2, tgt_hidden=256, hidden=512, n_layers=2, n_kv_heads=1, head_dim=0, latent_dim=512,
                  rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=7)
 
@@ -77,6 +83,9 @@ PROJ_CASES = [
     ("gqa64-B37-tiled", GQA_G64, 37, RopeSpec(theta=1e6, rot=64)),
     ("gqa256-B3", GQA_G256, 3, RopeSpec(theta=1e4, rot=256)),
     ("gqa256-B30-tiled", GQA_G256, 30, RopeSpec(theta=1e4, rot=256)),
+    ("gqaW640-B40", GQA_W1, 40, RopeSpec(theta=1e6, rot=64)),
+    ("gqaW640-B70", GQA_W1, 70, RopeSpec(theta=1e6, rot=64)),
+    ("gqaW1280-B130", GQA_W2, 130, RopeSpec(theta=1e6, rot=64, yarn=True, factor=4.0, orig_ctx=1024.0)),
     ("mla-B1", MLA_G, 1, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
     ("mla-B3", MLA_G, 3, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
     ("mla-B33-tiled", MLA_G, 33, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
