@@ -190,6 +190,109 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
     }
 }
 
+// GQA with k_norm + RoPE, vectorised: one workgroup per token row; thread t takes the row's 16-byte
+// chunks t, t + 512, t + 1024 (K chunks of every layer first, then the V chunks), all loaded before
+// any is used.  A K head of hd elements is hd/8 consecutive lanes of one wave: its sum of squares
+// is a butterfly over those lanes, and the NeoX partner of chunk q (elements j and j + hd/2) is the
+// lane hd/16 away, whose normalised values come over by lane exchange.  The per-element arithmetic
+// is that of knorm_rope_head; only the order in which the squares are summed differs.
+constexpr int kFinVThreads = 512;
+constexpr int kFinVPer = 3;
+
+__global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizeParams p) {
+    const int row = blockIdx.x;
+    const int r = row / p.W, i = row - (row / p.W) * p.W;
+    const int tid = threadIdx.x;
+
+    if (p.advance && i == 0) request_advance(p, r);
+    int64_t slot = -1;
+    const bool w = p.store && row_destination(p, r, i, row, slot);
+    if (p.store && tid == 0) {
+        p.slot[row] = slot;
+        p.wmask[row] = w ? 1 : 0;
+    }
+    const int64_t dst0 = w ? slot_offset(p, slot) : 0;
+    uint16_t *const out_row = p.kv_out ? p.kv_out + (int64_t)row * p.O : nullptr;
+
+    const int hd = p.hd, half = hd >> 1;
+    const int qh = hd >> 3, hq = qh >> 1;   // chunks per head, per half head
+    const int lch = p.nkv * qh;             // K (or V) chunks of one layer
+    const int kch = p.L * lch;              // K chunks of the row; as many V chunks follow
+    const int nch = 2 * kch;
+    const float *cs = rope_row(p.nr, row);
+
+    for (int base = 0; base < nch; base += kFinVThreads * kFinVPer) {
+        u32x4 y[kFinVPer], wk[kFinVPer];
+        f32x4 cv[kFinVPer][2], sv[kFinVPer][2];
+        int64_t col[kFinVPer], dst[kFinVPer];
+        uint16_t *pool[kFinVPer];
+        bool isk[kFinVPer], ok[kFinVPer];
+        // every load of this pass first
+#pragma unroll
+        for (int m = 0; m < kFinVPer; ++m) {
+            const int c = base + m * kFinVThreads + tid;
+            ok[m] = c < nch;
+            isk[m] = c < kch;
+            const int cc = !ok[m] ? 0 : isk[m] ? c : c - kch;
+            const int l = cc / lch, rem = cc - l * lch;
+            const int h = rem / qh, q = rem - h * qh;
+            col[m] = (int64_t)l * p.per_layer + (isk[m] ? 0 : p.nkv * hd) + rem * 8;
+            dst[m] = dst0 + (int64_t)h * p.sh + q * 8;
+            pool[m] = isk[m] ? p.pk[l] : p.pv[l];
+            y[m] = ok[m] ? load_y8(p, row, col[m]) : u32x4{0u, 0u, 0u, 0u};
+            wk[m] = u32x4{0u, 0u, 0u, 0u};
+            if (ok[m] && isk[m]) {
+                wk[m] = *(const u32x4 *)(p.nr.w_knorm + (int64_t)l * hd + q * 8);
+                const int j0 = (q < hq ? q : q - hq) * 8;
+                cv[m][0] = *(const f32x4 *)(cs + j0);
+                cv[m][1] = *(const f32x4 *)(cs + j0 + 4);
+                sv[m][0] = *(const f32x4 *)(cs + half + j0);
+                sv[m][1] = *(const f32x4 *)(cs + half + j0 + 4);
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < kFinVPer; ++m) {
+            // sum of squares over the head's lanes (every lane takes part in the exchanges)
+            float v8[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v8[2 * e] = bf_lo(y[m][e]);
+                v8[2 * e + 1] = bf_hi(y[m][e]);
+            }
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ss += v8[e] * v8[e];
+            for (int off = hq; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+            const float rinv = 1.0f / sqrtf(ss / (float)hd + p.nr.eps);
+            // normalised values, rounded to bf16, and the partner's
+            uint32_t u2[4], pu2[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                u2[e] = pack2(bf_lo(wk[m][e]) * (v8[2 * e] * rinv), bf_hi(wk[m][e]) * (v8[2 * e + 1] * rinv));
+                pu2[e] = (uint32_t)__shfl_xor((int)u2[e], hq, kWave);
+            }
+            if (!ok[m]) continue;
+            u32x4 o = y[m];
+            if (isk[m]) {
+                const int c = base + m * kFinVThreads + tid;
+                const bool first = ((c % qh) < hq);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float cl = cv[m][e >> 1][(2 * e) & 3], ch = cv[m][e >> 1][(2 * e + 1) & 3];
+                    const float sl = sv[m][e >> 1][(2 * e) & 3], sh = sv[m][e >> 1][(2 * e + 1) & 3];
+                    const float ul = bf_lo(u2[e]), uh = bf_hi(u2[e]), pl = bf_lo(pu2[e]), ph = bf_hi(pu2[e]);
+                    // first half: k = u c - u' s; second half: k = u c + u' s (u' the partner)
+                    const float kl = first ? ul * cl - pl * sl : ul * cl + pl * sl;
+                    const float kh = first ? uh * ch - ph * sh : uh * ch + ph * sh;
+                    o[e] = pack2(kl, kh);
+                }
+            }
+            if (out_row) *(u32x4 *)(out_row + col[m]) = o;
+            if (w) *(u32x4 *)(pool[m] + dst[m]) = o;
+        }
+    }
+}
+
 // Advance only: one workgroup per request.
 __global__ __launch_bounds__(64) void k_advance(const FinalizeParams p) { request_advance(p, blockIdx.x); }
 
@@ -240,6 +343,9 @@ hipError_t launch_store_rows(const FinalizeParams &p, hipStream_t s) {
 hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s) {
     const int64_t N = (int64_t)p.B * p.W;
     if (N == 0) return hipSuccess;
+    // the vectorised GQA kernel reads k_norm weights and cos/sin in 16-byte pieces
+    if (p.norm && p.kind == DFKV_GQA && ((uintptr_t)p.nr.w_knorm & 15u) == 0 && ((uintptr_t)p.nr.cos_sin & 15u) == 0)
+        return launch1(k_finalize_gqa, dim3((unsigned)N), dim3(kFinVThreads), s, p);
     return launch1(k_finalize, dim3((unsigned)N), dim3(kFinThreads), s, p);
 }
 

@@ -179,3 +179,33 @@ def test_norm_rope_far_positions(orc, kind):
     torch.cuda.synchronize()
     want = orc.norm_rope(geom, y, wl.w_knorm, wl.ctx_len, orc.rope_cache(rope, wl.cache_len))
     assert_close_bf16(ds.bits(ds.kv_out), want, "norm_rope far positions")
+
+
+@pytest.mark.parametrize("geom,B", [(GQA_W1, 40), (GQA_G, 30)], ids=["gqaW640-B40", "gqa128-B30"])
+def test_finalize_unaligned_operands(orc, geom, B):
+    """k_norm weights and the cos/sin cache only as aligned as the interface requires (2 and 4 bytes):
+    the finalize reads them element by element instead of in 16-byte pieces, with the same result
+    against the oracle."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    rope = RopeSpec(theta=1e6, rot=geom.rope_dim)
+    wl, ds, ref = _run_case(orc, "unaligned", geom, B, rope)
+    ds.kv_out.fill_(0x7FC0)
+    ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    assert_close_bf16(ds.bits(ds.kv_out), ref["kv"], "aligned")
+    w_fc, w_hn, w_kv, w_kn = ds.weights[0]
+    kn_buf = torch.zeros(w_kn.numel() + 8, dtype=w_kn.dtype, device=w_kn.device)
+    kn_mis = kn_buf[1:1 + w_kn.numel()].view(w_kn.shape)
+    kn_mis.copy_(w_kn)
+    cs = ds.cos_sin
+    cs_buf = torch.zeros(cs.numel() + 4, dtype=cs.dtype, device=cs.device)
+    cs_mis = cs_buf[1:1 + cs.numel()].view(cs.shape)
+    cs_mis.copy_(cs)
+    assert kn_mis.data_ptr() % 16 == 2 and cs_mis.data_ptr() % 16 == 4
+    ds.weight_structs[0] = dfkv.make_weights(w_fc, w_hn, w_kv, kn_mis)
+    ds.cos_sin = cs_mis
+    ds.kv_out.fill_(0x7FC0)
+    ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    assert_close_bf16(ds.bits(ds.kv_out), ref["kv"], "unaligned")
