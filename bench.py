@@ -411,7 +411,7 @@ def main() -> int:
         achieved = alg["fc_flops"] / (fc_mean * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
-                    kernel="k_gemm (dfkv_project_fc: the fc GEMM) + k_hidden_norm",
+                    kernel="k_gemm (dfkv_project_fc: the fc GEMM on the packed w_fc) + k_hidden_norm",
                     algorithmic_flops_per_launch=alg["fc_flops"])
     roof.update(launch_us_mean=round(fc_mean, 2), launch_us_p10=round(float(np.percentile(fc_us, 10)), 2),
                 launch_us_p90=round(float(np.percentile(fc_us, 90)), 2))

@@ -108,12 +108,18 @@ typedef struct dfkv_geom {
  *  w_fc    [hidden][n_tgt * tgt_hidden]
  *  w_hnorm [hidden]
  *  w_kv    [n_layers * per_layer][hidden]  (per_layer = 2*nkv*hd or R+P)
- *  w_knorm [n_layers][head_dim] (GQA k_norm) or [n_layers][latent_dim] (MLA) */
+ *  w_knorm [n_layers][head_dim] (GQA k_norm) or [n_layers][latent_dim] (MLA)
+ *  w_fc_packed  NULL, or the copy of w_fc that dfkv_pack_fc_weight wrote (same
+ *          size, 16-byte aligned): above 64 rows the fc GEMM then reads it
+ *          instead of w_fc, with the same result bit for bit (only the order of
+ *          its bytes in memory differs).  w_fc itself is still required: at
+ *          64 rows or fewer the fc streams w_fc. */
 typedef struct dfkv_weights {
     const void *w_fc;
     const void *w_hnorm;
     const void *w_kv;
     const void *w_knorm;
+    const void *w_fc_packed;
 } dfkv_weights;
 
 /* Request state of one step (all device arrays).
@@ -241,6 +247,21 @@ dfkv_status dfkv_workspace_init(void *ws, size_t ws_bytes, dfkv_stream_t stream)
 dfkv_status dfkv_rope_cache_build(const dfkv_rope *rope, float *cos_sin, int32_t cache_len,
                                   dfkv_stream_t stream);
 
+/* Write w_fc (bf16 [hidden][n_tgt * tgt_hidden], 16-byte aligned) in the order
+ * the large-batch fc GEMM reads it: element (o, k) goes to bf16 index
+ *   ((((o/64) * (K/64) + k/64) * 4 + s) * 2 + (o/32)%2) * 512 + (o%32 + 32*h) * 8 + e,
+ * K = n_tgt*tgt_hidden, k%64 = 32*h + 8*s + e (h < 2, s < 4, e < 8): the fragments
+ * the 64 lanes of one wave load for one MFMA step sit in 1 KB in a row.  Done once
+ * per weight (weights are static); put the result in dfkv_weights.w_fc_packed.
+ * A memory layout of this library for the MI355X matrix cores, not an operation
+ * of the method: the GEMM's arithmetic is unchanged.
+ * For callers that keep one copy of w_fc: the large-batch path only needs the
+ * packed copy, the small-batch path (<= 64 rows) only the row-major one.
+ *  w_fc_packed: device memory of hidden*K*2 bytes, 16-byte aligned; must not
+ *               overlap w_fc.
+ * Errors: NULL; SHAPE (geometry); LAYOUT (alignment); ALIAS; HIP. */
+dfkv_status dfkv_pack_fc_weight(const dfkv_geom *g, const void *w_fc, void *w_fc_packed, dfkv_stream_t stream);
+
 /* Context projection of all N = n_reqs*W rows ([P20550]
  * TLLM_DFLASH_OVERLAP_CONTEXT_PROJECTION: fc + hidden_norm + latent GEMM +
  * RMSNorm/RoPE; [P13995] one GEMM stacked across drafter layers).
@@ -268,12 +289,12 @@ dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *
  * workspace).
  * dfkv_project_fc: f = bf16(hidden . w_fc^T) and what hidden_norm needs of it
  *   (its row statistics and w_hnorm-weighted copy, or the normalised rows) into
- *   ws.  Reads hidden, w_fc and w_hnorm only.
+ *   ws.  Reads hidden, w_fc (or w_fc_packed) and w_hnorm only.
  * dfkv_project_kv: from what dfkv_project_fc left in ws (same geometry and
  *   n_reqs): hidden_norm, the stacked GEMM and, with DFKV_FUSE_NORM_ROPE,
  *   k_norm + RoPE into kv_out.
  * Arguments, layouts and errors as dfkv_project. */
-dfkv_status dfkv_project_fc(const dfkv_geom *g, const void *w_fc, const void *w_hnorm, const void *hidden,
+dfkv_status dfkv_project_fc(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
                             int64_t hidden_row_stride, int32_t n_reqs, void *ws, size_t ws_bytes,
                             dfkv_stream_t stream);
 dfkv_status dfkv_project_kv(const dfkv_geom *g, const dfkv_weights *w, int32_t n_reqs, const int32_t *ctx_len_in,

@@ -204,8 +204,12 @@ dfkv_status check_project(const dfkv_geom *g, const dfkv_weights *w, const void 
     if (!al16(hidden) || !al16(kv_out) || !al16(w->w_fc) || !al16(w->w_hnorm) || !al16(w->w_kv) || !al16(ws))
         return DFKV_ERR_LAYOUT;
     if (fuse && (!al4(cs) || ((uintptr_t)w->w_knorm & 1u))) return DFKV_ERR_LAYOUT;
+    if (w->w_fc_packed && !al16(w->w_fc_packed)) return DFKV_ERR_LAYOUT;
     if (ws_bytes < pl->total) return DFKV_ERR_WORKSPACE;
     const size_t kv_bytes = (size_t)M * O * 2;
+    if (w->w_fc_packed && (overlap(kv_out, kv_bytes, w->w_fc_packed, (size_t)H * K * 2) ||
+                           overlap(ws, ws_bytes, w->w_fc_packed, (size_t)H * K * 2)))
+        return DFKV_ERR_ALIAS;
     const size_t hid_bytes = (size_t)((M - 1) * ld + K) * 2;
     if (overlap(kv_out, kv_bytes, hidden, hid_bytes) || overlap(kv_out, kv_bytes, ws, ws_bytes) ||
         overlap(kv_out, kv_bytes, w->w_fc, (size_t)H * K * 2) || overlap(kv_out, kv_bytes, w->w_kv, (size_t)O * H * 2) ||
@@ -406,8 +410,8 @@ FinalizeParams fin_params(const dfkv_geom *g, const dfkv_requests *r, const dfkv
 // asks for it, the paged store and the advance.
 bool stages_g(const Plan &pl) { return pl.skinny && pl.M <= 16; }
 
-dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int64_t ld, const void *w_hnorm,
-                   void *ws, const Plan &pl, hipStream_t s) {
+dfkv_status run_fc(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t ld, void *ws,
+                   const Plan &pl, hipStream_t s) {
     if (pl.M == 0) return DFKV_OK;
     char *wsb = (char *)ws;
     const int64_t K = k_in(g), H = g->hidden;
@@ -416,7 +420,7 @@ dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int
     if (pl.skinny) {
         StreamParams p;
         memset(&p, 0, sizeof p);
-        p.w = (const uint16_t *)w_fc;
+        p.w = (const uint16_t *)w->w_fc;
         p.x = (const uint16_t *)hidden;
         p.ldx = ld;
         p.M = (int32_t)pl.M;
@@ -429,8 +433,9 @@ dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int
         e = launch_stream(p, s);
     } else {
         float *part = pl.S_fc > 1 ? (float *)(wsb + pl.off_part) : nullptr;
-        GemmParams t{(const uint16_t *)hidden, ld, (const uint16_t *)w_fc, f, H, part, (int32_t)pl.M, (int32_t)K,
-                     (int32_t)H, (int32_t)pl.S_fc};
+        const bool packed = w->w_fc_packed != nullptr;
+        GemmParams t{(const uint16_t *)hidden, ld, (const uint16_t *)(packed ? w->w_fc_packed : w->w_fc), f, H, part,
+                     (int32_t)pl.M, (int32_t)K, (int32_t)H, (int32_t)pl.S_fc, packed ? 1 : 0};
         e = launch_gemm(t, s);
     }
     if (e != hipSuccess) return hip_status(e);
@@ -438,7 +443,7 @@ dfkv_status run_fc(const dfkv_geom *g, const void *w_fc, const void *hidden, int
     uint16_t *gb = (uint16_t *)(wsb + pl.off_g);
     const float *part = !pl.skinny && pl.S_fc > 1 ? (const float *)(wsb + pl.off_part) : nullptr;
     return hip_status(
-        launch_hidden_norm(f, part, pl.S_fc, (const uint16_t *)w_hnorm, gb, (int)pl.M, (int)H, g->eps, pl.kv_w, s));
+        launch_hidden_norm(f, part, pl.S_fc, (const uint16_t *)w->w_hnorm, gb, (int)pl.M, (int)H, g->eps, pl.kv_w, s));
 }
 
 dfkv_status run_kvfin(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx, const float *cs,
@@ -537,7 +542,7 @@ dfkv_status run_project(const dfkv_geom *g, const dfkv_weights *w, const void *h
                         const float *cs, int32_t cache_len, void *kv_out, bool fuse, void *ws, const Plan &pl,
                         const FinalizeParams &fin, bool need_finalize, hipStream_t s) {
     if (pl.M == 0) return DFKV_OK;
-    dfkv_status st = run_fc(g, w->w_fc, hidden, ld, w->w_hnorm, ws, pl, s);
+    dfkv_status st = run_fc(g, w, hidden, ld, ws, pl, s);
     if (st != DFKV_OK) return st;
     return run_kv(g, w, ctx, cs, cache_len, kv_out, fuse, ws, pl, fin, need_finalize, s);
 }
@@ -666,24 +671,36 @@ dfkv_status dfkv_join(dfkv_stream_t main, void *join) {
     return hip_status(hipStreamWaitEvent((hipStream_t)main, (hipEvent_t)join, 0));
 }
 
-dfkv_status dfkv_project_fc(const dfkv_geom *g, const void *w_fc, const void *w_hnorm, const void *hidden,
+dfkv_status dfkv_project_fc(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
                             int64_t hidden_row_stride, int32_t n_reqs, void *ws, size_t ws_bytes,
                             dfkv_stream_t stream) {
-    if (!g) return DFKV_ERR_NULL;
+    if (!g || !w) return DFKV_ERR_NULL;
     Plan pl;
     dfkv_status st = make_plan(g, n_reqs, &pl);
     if (st != DFKV_OK) return st;
     if (pl.M == 0) return DFKV_OK;
-    if (!w_fc || !hidden || !ws || !w_hnorm) return DFKV_ERR_NULL;
+    if (!w->w_fc || !hidden || !ws || !w->w_hnorm) return DFKV_ERR_NULL;
     const int64_t K = k_in(g), H = g->hidden, M = pl.M;
     if (hidden_row_stride < K || (hidden_row_stride * 2) % 16 != 0) return DFKV_ERR_LAYOUT;
-    if (!al16(hidden) || !al16(w_fc) || !al16(ws) || !al16(w_hnorm)) return DFKV_ERR_LAYOUT;
+    if (!al16(hidden) || !al16(w->w_fc) || !al16(ws) || !al16(w->w_hnorm)) return DFKV_ERR_LAYOUT;
+    if (w->w_fc_packed && !al16(w->w_fc_packed)) return DFKV_ERR_LAYOUT;
     if (ws_bytes < pl.total) return DFKV_ERR_WORKSPACE;
     const size_t hid_bytes = (size_t)((M - 1) * hidden_row_stride + K) * 2;
-    if (overlap(ws, ws_bytes, hidden, hid_bytes) || overlap(ws, ws_bytes, w_fc, (size_t)H * K * 2) ||
-        overlap(ws, ws_bytes, w_hnorm, (size_t)H * 2))
+    if (overlap(ws, ws_bytes, hidden, hid_bytes) || overlap(ws, ws_bytes, w->w_fc, (size_t)H * K * 2) ||
+        overlap(ws, ws_bytes, w->w_hnorm, (size_t)H * 2) ||
+        (w->w_fc_packed && overlap(ws, ws_bytes, w->w_fc_packed, (size_t)H * K * 2)))
         return DFKV_ERR_ALIAS;
-    return run_fc(g, w_fc, hidden, hidden_row_stride, w_hnorm, ws, pl, (hipStream_t)stream);
+    return run_fc(g, w, hidden, hidden_row_stride, ws, pl, (hipStream_t)stream);
+}
+
+dfkv_status dfkv_pack_fc_weight(const dfkv_geom *g, const void *w_fc, void *w_fc_packed, dfkv_stream_t stream) {
+    if (!g || !w_fc || !w_fc_packed) return DFKV_ERR_NULL;
+    dfkv_status st = check_geom(g);
+    if (st != DFKV_OK) return st;
+    if (!al16(w_fc) || !al16(w_fc_packed)) return DFKV_ERR_LAYOUT;
+    const int64_t K = k_in(g), H = g->hidden;
+    if (overlap(w_fc, (size_t)H * K * 2, w_fc_packed, (size_t)H * K * 2)) return DFKV_ERR_ALIAS;
+    return hip_status(launch_pack_rows((const uint16_t *)w_fc, (uint16_t *)w_fc_packed, H, K, (hipStream_t)stream));
 }
 
 dfkv_status dfkv_project_kv(const dfkv_geom *g, const dfkv_weights *w, int32_t n_reqs, const int32_t *ctx_len_in,

@@ -137,6 +137,8 @@ hipError_t launch_bt_decode(const BtDecodeArgs &a, hipStream_t s);
 hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint16_t *w, uint16_t *g, int n_rows,
                               int H, float eps, bool packed, hipStream_t s);
 hipError_t launch_rope_cache(const dfkv_rope &r, float *cs, int cache_len, hipStream_t s);
+// dst = src [rows][K] (rows and K multiples of 64) in the fragment order of gemm_pack_index
+hipError_t launch_pack_rows(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t K, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
 // Weight-streaming projection GEMM (M <= 64 token rows).
@@ -192,6 +194,7 @@ struct GemmParams {
     int64_t ldo;
     float *part;
     int32_t M, K, O, S;
+    int32_t w_packed;   // k_gemm: w is packed in fragment order over the features (gemm_pack_index)
 };
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s);
 int gemm_tiles(int M, int O);   // output tiles of launch_gemm (times S workgroups)

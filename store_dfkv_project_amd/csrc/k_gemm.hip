@@ -61,6 +61,7 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // Wave w computes all 256 tokens x features w*64 .. +64.  k is permuted inside each 64-wide stage so
 // that a lane's weight fragment is 64 contiguous bytes: MFMA slice s, lane half h takes physical
 // k = 32 h + 8 s + (0..7), for both operands, which leaves every dot product unchanged.
+template <bool PACKED_W>
 __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[GSMEM];
 
@@ -100,12 +101,21 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
             __builtin_amdgcn_global_load_lds((const void *)(asrc[i] + k0), (lds_void *)(base + (i * 4 + wave) * 1024),
                                              16, 0, 0);
     };
-    // weight fragments: feature o0 + wave*64 + 32 j + fr, 16 bytes at physical k = k0 + 32 fh + 8 s
+    // weight fragments: feature o0 + wave*64 + 32 j + fr, 16 bytes at physical k = k0 + 32 fh + 8 s.
+    // Row-major weights: two rows per fragment load and lane pair.  Packed weights (gemm_pack_index
+    // over the features): the 64 lanes' fragments of one (block, stage, slice, j) are 1 KB in a row.
     const uint16_t *bsrc[GFN];
+    const uint8_t *bpk;
+    if (PACKED_W) {
+        const int nblk = (p.O + 63) >> 6;
+        const int b = (o0 >> 6) + wave < nblk ? (o0 >> 6) + wave : nblk - 1;
+        bpk = (const uint8_t *)p.w + ((int64_t)b * iters * 512 + lane) * 16;
+    } else {
 #pragma unroll
-    for (int j = 0; j < GFN; ++j) {
-        const int o = o0 + wave * 64 + 32 * j + fr;
-        bsrc[j] = p.w + (int64_t)(o < p.O ? o : p.O - 1) * p.K + 32 * fh;
+        for (int j = 0; j < GFN; ++j) {
+            const int o = o0 + wave * 64 + 32 * j + fr;
+            bsrc[j] = p.w + (int64_t)(o < p.O ? o : p.O - 1) * p.K + 32 * fh;
+        }
     }
     // The weight loads are inline assembly, waited for by hand with the counts below: the compiler's
     // own wait insertion cannot follow them around the loop next to the loads into LDS and would wait
@@ -113,10 +123,12 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
     // of them can move above it.
     u32x4 bw[GNS][GFN];
     auto load_b = [&](int it, int s) {
-        const int k0 = it * GBK + 8 * s;
 #pragma unroll
-        for (int j = 0; j < GFN; ++j)
-            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bw[s][j]) : "v"(bsrc[j] + k0));
+        for (int j = 0; j < GFN; ++j) {
+            const void *src = PACKED_W ? (const void *)(bpk + (int64_t)((it * GNS + s) * GFN + j) * 1024)
+                                       : (const void *)(bsrc[j] + it * GBK + 8 * s);
+            asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(bw[s][j]) : "v"(src));
+        }
     };
     static_assert(GFN == 2, "the waits name GFN registers per slice");
     // token fragments of slice s from LDS: row 32 i + fr, physical chunk 4 fh + s
@@ -277,7 +289,11 @@ hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
     if (p.K % GBK != 0 || p.S < 1 || p.S > p.K / GBK || (p.S > 1 && !p.part) || (p.S == 1 && !p.part && !p.out))
         return hipErrorInvalidValue;
     const unsigned tiles = (unsigned)gemm_tiles(p.M, p.O);
-    return launch1(k_gemm, dim3(tiles * (unsigned)p.S), dim3(GTHREADS), s, p);
+    if (p.w_packed) {
+        if (p.O % 64 != 0) return hipErrorInvalidValue;
+        return launch1(k_gemm<true>, dim3(tiles * (unsigned)p.S), dim3(GTHREADS), s, p);
+    }
+    return launch1(k_gemm<false>, dim3(tiles * (unsigned)p.S), dim3(GTHREADS), s, p);
 }
 
 }  // namespace dfkv

@@ -94,6 +94,31 @@ hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint1
 }
 
 // ---------------------------------------------------------------------------
+// A row-major bf16 matrix [rows][K] rewritten in the fragment order of
+// gemm_pack_index (the large-batch GEMM's per-wave operand): one thread per
+// 16-byte chunk, which moves whole (8 consecutive k stay together).
+// ---------------------------------------------------------------------------
+struct PackArgs {
+    const uint16_t *src;
+    uint16_t *dst;
+    int64_t rows, K;
+};
+
+__global__ __launch_bounds__(256) void k_pack_rows(const PackArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t cpr = a.K >> 3;
+    if (t >= a.rows * cpr) return;
+    const int64_t n = t / cpr, c = t - n * cpr;
+    *(u32x4 *)(a.dst + gemm_pack_index(n, c << 3, a.K >> 6)) = *(const u32x4 *)(a.src + n * a.K + (c << 3));
+}
+
+hipError_t launch_pack_rows(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t K, hipStream_t s) {
+    if (rows % 64 != 0 || K % 64 != 0 || rows <= 0) return hipErrorInvalidValue;
+    const int64_t chunks = rows * (K >> 3);
+    return launch1(k_pack_rows, dim3((unsigned)((chunks + 255) / 256)), dim3(256), s, PackArgs{src, dst, rows, K});
+}
+
+// ---------------------------------------------------------------------------
 // cos/sin cache in fp64 (stored fp32).  Plain RoPE: inv_i = theta^(-2i/rot).
 // YaRN (Peng et al. 2023, "NTK-by-parts" + attention temperature, in the HF
 // formulation that honours truncate=false): the correction dim for n turns is

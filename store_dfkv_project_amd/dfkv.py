@@ -35,7 +35,7 @@ DFKV_FUSE_NORM_ROPE = 1
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
             "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join", "dfkv_block_table_decode",
-            "dfkv_strict_accept", "dfkv_paged_store_rows")
+            "dfkv_strict_accept", "dfkv_paged_store_rows", "dfkv_pack_fc_weight")
 
 
 class dfkv_geom(C.Structure):
@@ -46,7 +46,8 @@ class dfkv_geom(C.Structure):
 
 
 class dfkv_weights(C.Structure):
-    _fields_ = [("w_fc", C.c_void_p), ("w_hnorm", C.c_void_p), ("w_kv", C.c_void_p), ("w_knorm", C.c_void_p)]
+    _fields_ = [("w_fc", C.c_void_p), ("w_hnorm", C.c_void_p), ("w_kv", C.c_void_p), ("w_knorm", C.c_void_p),
+                ("w_fc_packed", C.c_void_p)]
 
 
 class dfkv_requests(C.Structure):
@@ -107,7 +108,8 @@ def _load() -> C.CDLL:
         "dfkv_workspace_init": ([P, SZ, P], C.c_int),
         "dfkv_rope_cache_build": ([C.POINTER(dfkv_rope), P, I32, P], C.c_int),
         "dfkv_project": ([gp, wp, P, I64, I32, P, P, I32, P, U32, P, SZ, P], C.c_int),
-        "dfkv_project_fc": ([gp, P, P, P, I64, I32, P, SZ, P], C.c_int),
+        "dfkv_project_fc": ([gp, wp, P, I64, I32, P, SZ, P], C.c_int),
+        "dfkv_pack_fc_weight": ([gp, P, P, P], C.c_int),
         "dfkv_project_kv": ([gp, wp, I32, P, P, I32, P, U32, P, SZ, P], C.c_int),
         "dfkv_norm_rope": ([gp, P, I32, P, P, I32, P, P], C.c_int),
         "dfkv_paged_store": ([gp, P, rp, pp, P, P, P], C.c_int),
@@ -178,8 +180,8 @@ def make_geom(**kw) -> dfkv_geom:
     return g
 
 
-def make_weights(w_fc, w_hnorm, w_kv, w_knorm) -> dfkv_weights:
-    return dfkv_weights(_ptr(w_fc), _ptr(w_hnorm), _ptr(w_kv), _ptr(w_knorm))
+def make_weights(w_fc, w_hnorm, w_kv, w_knorm, w_fc_packed=None) -> dfkv_weights:
+    return dfkv_weights(_ptr(w_fc), _ptr(w_hnorm), _ptr(w_kv), _ptr(w_knorm), _ptr(w_fc_packed))
 
 
 def make_requests(n_reqs, ctx_len_in, n_acc, alloc_limit, is_dummy, row_valid, block_table, bt_row_stride, bt_cols,
@@ -287,9 +289,14 @@ def dfkv_join(main, join) -> None:
     _check(_lib.dfkv_join(_stream(main), C.c_void_p(join)), "dfkv_join")
 
 
-def dfkv_project_fc(geom, w_fc, w_hnorm, hidden, hidden_row_stride, n_reqs, ws, ws_bytes, stream=None) -> None:
-    _check(_lib.dfkv_project_fc(_ref(geom), _ptr(w_fc), _ptr(w_hnorm), _ptr(hidden), int(hidden_row_stride),
-                                int(n_reqs), _ptr(ws), int(ws_bytes), _stream(stream)), "dfkv_project_fc")
+def dfkv_project_fc(geom, weights, hidden, hidden_row_stride, n_reqs, ws, ws_bytes, stream=None) -> None:
+    _check(_lib.dfkv_project_fc(_ref(geom), _ref(weights), _ptr(hidden), int(hidden_row_stride), int(n_reqs),
+                                _ptr(ws), int(ws_bytes), _stream(stream)), "dfkv_project_fc")
+
+
+def dfkv_pack_fc_weight(geom, w_fc, w_fc_packed, stream=None) -> None:
+    _check(_lib.dfkv_pack_fc_weight(_ref(geom), _ptr(w_fc), _ptr(w_fc_packed), _stream(stream)),
+           "dfkv_pack_fc_weight")
 
 
 def dfkv_project_kv(geom, weights, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out, flags, ws, ws_bytes,

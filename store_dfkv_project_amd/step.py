@@ -42,10 +42,12 @@ class DeviceStep:
     pool_layout: "nhd" ([page][slot][head][dim]) or "hnd" ([page][head][slot][dim]); MLA pools are
     [page][slot][R+P].  weight_copies > 1 keeps that many copies of the weights at distinct addresses
     (so that a timing loop can rotate through them and read them from HBM, not from the cache).
+    pack_fc: also give each copy a packed fc weight (dfkv_pack_fc_weight), which the large-batch fc
+    GEMM then reads.
     """
 
     def __init__(self, wl, device: str = "cuda", pool_layout: str = "nhd", weight_copies: int = 1,
-                 pool_seed: int = 1234, with_weights: bool = True):
+                 pool_seed: int = 1234, with_weights: bool = True, pack_fc: bool = True):
         self.wl = wl
         g = wl.geom
         self.geom = g
@@ -58,13 +60,19 @@ class DeviceStep:
         # projection inputs
         self.hidden = _dev(wl.hidden, device)
         self.weights = []
+        self.w_fc_packed = []
         self.weight_structs = []
         if with_weights and wl.w_fc is not None:
             base = [_dev(wl.w_fc, device), _dev(wl.w_hnorm, device), _dev(wl.w_kv, device), _dev(wl.w_knorm, device)]
             for c in range(weight_copies):
                 ws = base if c == 0 else [t.clone() for t in base]
                 self.weights.append(ws)
-                self.weight_structs.append(dfkv.make_weights(*ws))
+                pk = None
+                if pack_fc:
+                    pk = torch.empty_like(ws[0])
+                    dfkv.dfkv_pack_fc_weight(self.gs, ws[0], pk)
+                self.w_fc_packed.append(pk)
+                self.weight_structs.append(dfkv.make_weights(*ws, w_fc_packed=pk))
         # request state
         self.ctx_len = _dev(wl.ctx_len.astype(np.int32), device)
         self.n_acc = _dev(wl.n_acc.astype(np.int32), device)
@@ -144,9 +152,8 @@ class DeviceStep:
                                self.ws, self.ws_bytes, main, aux, fork, join)
 
     def project_fc(self, copy: int = 0, stream=None):
-        w = self.weights[copy]
-        dfkv.dfkv_project_fc(self.gs, w[0], w[1], self.hidden, self.wl.hidden_row_stride, self.wl.n_reqs, self.ws,
-                             self.ws_bytes, stream)
+        dfkv.dfkv_project_fc(self.gs, self.weight_structs[copy], self.hidden, self.wl.hidden_row_stride,
+                             self.wl.n_reqs, self.ws, self.ws_bytes, stream)
 
     def project_kv(self, flags: int = dfkv.DFKV_FUSE_NORM_ROPE, copy: int = 0, stream=None):
         dfkv.dfkv_project_kv(self.gs, self.weight_structs[copy], self.wl.n_reqs, self.ctx_len, self.cos_sin,

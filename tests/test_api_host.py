@@ -121,6 +121,35 @@ def test_project_validation(over, want):
     assert status_of(dfkv.dfkv_project, **project_args(**over)) == want
 
 
+def test_pack_fc_weight_validation():
+    f = dfkv.dfkv_pack_fc_weight
+    assert status_of(f, geom(), None, addr(2)) == dfkv.DFKV_ERR_NULL
+    assert status_of(f, geom(), addr(1), None) == dfkv.DFKV_ERR_NULL
+    assert dfkv.lib().dfkv_pack_fc_weight(None, addr(1), addr(2), None) == dfkv.DFKV_ERR_NULL
+    assert status_of(f, geom(hidden=4000), addr(1), addr(2)) == dfkv.DFKV_ERR_SHAPE
+    assert status_of(f, geom(), addr(1) + 8, addr(2)) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(f, geom(), addr(1), addr(2) + 2) == dfkv.DFKV_ERR_LAYOUT
+    # the packed copy over the row-major one
+    assert status_of(f, geom(), addr(1), addr(1) + 1024) == dfkv.DFKV_ERR_ALIAS
+
+
+def test_project_packed_weight_checks():
+    ok_ws = dfkv.dfkv_workspace_size(geom(), 1)
+    w = lambda pk: dfkv.make_weights(addr(1), addr(2), addr(3), addr(4), w_fc_packed=pk)
+    assert status_of(dfkv.dfkv_project, **project_args(weights=w(addr(10) + 8), ws_bytes=ok_ws)) == dfkv.DFKV_ERR_LAYOUT
+    # the packed weight over kv_out, or inside the workspace
+    assert status_of(dfkv.dfkv_project, **project_args(weights=w(addr(8)), ws_bytes=ok_ws)) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(dfkv.dfkv_project, **project_args(weights=w(addr(9) + 256), ws_bytes=ok_ws)) == \
+        dfkv.DFKV_ERR_ALIAS
+    # the fc stage alone takes the same weights struct
+    fc = dict(geom=geom(), weights=w(addr(10)), hidden=addr(5), hidden_row_stride=12288, n_reqs=1, ws=addr(9),
+              ws_bytes=ok_ws, stream=0)
+    assert status_of(dfkv.dfkv_project_fc, **dict(fc, weights=None)) == dfkv.DFKV_ERR_NULL
+    assert status_of(dfkv.dfkv_project_fc, **dict(fc, weights=w(addr(10) + 2))) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(dfkv.dfkv_project_fc, **dict(fc, weights=w(addr(9)))) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(dfkv.dfkv_project_fc, **dict(fc, ws_bytes=ok_ws - 256)) == dfkv.DFKV_ERR_WORKSPACE
+
+
 def test_project_alias_checks():
     ok_ws = dfkv.dfkv_workspace_size(geom(), 1)
     # kv_out inside the hidden rows

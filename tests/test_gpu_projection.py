@@ -203,9 +203,58 @@ def test_finalize_unaligned_operands(orc, geom, B):
     cs_mis = cs_buf[1:1 + cs.numel()].view(cs.shape)
     cs_mis.copy_(cs)
     assert kn_mis.data_ptr() % 16 == 2 and cs_mis.data_ptr() % 16 == 4
-    ds.weight_structs[0] = dfkv.make_weights(w_fc, w_hn, w_kv, kn_mis)
+    ds.weight_structs[0] = dfkv.make_weights(w_fc, w_hn, w_kv, kn_mis, w_fc_packed=ds.w_fc_packed[0])
     ds.cos_sin = cs_mis
     ds.kv_out.fill_(0x7FC0)
     ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
     torch.cuda.synchronize()
     assert_close_bf16(ds.bits(ds.kv_out), ref["kv"], "unaligned")
+
+
+@pytest.mark.parametrize("H,K", [(256, 512), (384, 768), (4096, 12288)])
+def test_pack_fc_weight_layout(H, K):
+    """dfkv_pack_fc_weight puts element (o, k) where the header's formula says: checked against the same
+    permutation written as a reshape of the [H][K] matrix."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    from store_dfkv_project_amd.step import geom_struct
+    g = Geometry(kind=GQA, n_tgt=1, tgt_hidden=K, hidden=H, n_layers=1, n_kv_heads=1, head_dim=64, latent_dim=0,
+                 rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(H + K)
+    w = torch.randint(-32768, 32768, (H, K), dtype=torch.int16, device="cuda", generator=gen)
+    pk = torch.empty_like(w)
+    dfkv.dfkv_pack_fc_weight(geom_struct(g), w, pk)
+    torch.cuda.synchronize()
+    # o = 64 b + 32 j + fr, k = 64 it + 32 h + 8 s + e  ->  [b][it][s][j][h][fr][e]
+    want = w.view(H // 64, 2, 32, K // 64, 2, 4, 8).permute(0, 3, 5, 1, 4, 2, 6).reshape(H, K)
+    assert torch.equal(pk, want)
+
+
+PACK_CASES = [("gqa128-B30", GQA_G, 30), ("gqaW640-B70", GQA_W1, 70), ("mla-B33", MLA_G, 33), ("gqa64-B37", GQA_G64, 37)]
+
+
+@pytest.mark.parametrize("name,geom,B", PACK_CASES, ids=[c[0] for c in PACK_CASES])
+def test_packed_fc_weight_same_bits(orc, name, geom, B):
+    """Above 64 rows the fc GEMM reads the packed weight when given one: the projection (whole and
+    staged) is bit for bit the one from the row-major weight, and matches the oracle."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    rope = RopeSpec(theta=1e6, rot=geom.rope_dim)
+    wl, ds, ref = _run_case(orc, name, geom, B, rope)
+    assert ds.w_fc_packed[0] is not None
+    ds.kv_out.fill_(0x7FC0)
+    ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    packed = ds.kv_out.clone()
+    assert_close_bf16(ds.bits(packed), ref["kv"], f"{name} packed")
+    ds.kv_out.fill_(0x7FC0)
+    ds.project_fc()
+    ds.project_kv(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, ds.kv_out), "staged projection with the packed weight differs"
+    ds.weight_structs[0] = dfkv.make_weights(*ds.weights[0])
+    ds.kv_out.fill_(0x7FC0)
+    ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+    torch.cuda.synchronize()
+    assert torch.equal(packed, ds.kv_out), "packed and row-major fc weights give different bits"
