@@ -11,9 +11,8 @@ namespace dfkv {
 // workgroup per row (used by the large-batch path; the small-batch path folds
 // it into the stacked GEMM's operand load).  When the fc GEMM was split over
 // k, f is first formed here: f = bf16(sum over the S fp32 partials, in split
-// order), written out and then normalised.  With `packed`, g is written in the
-// fragment order of k_gemm_w's token operand (gemm_pack_index; H divides by 64)
-// and the rows up to the next multiple of 64 are zero.
+// order), written out and then normalised.  k_hidden_norm_packed (below) writes g
+// in the fragment order of k_gemm_w's token operand instead.
 // ---------------------------------------------------------------------------
 struct HiddenNormArgs {
     const uint16_t *w;
@@ -21,7 +20,7 @@ struct HiddenNormArgs {
     const float *part;   // [S][n_rows][H] fp32 partial sums of f, or null (f is given)
     int S, n_rows, H;
     float eps;
-    int packed;
+    int packed;          // rows per workgroup of k_hidden_norm_packed (0: row-major k_hidden_norm)
 };
 
 __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
@@ -30,15 +29,6 @@ __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
     const int H = a.H;
     const float eps = a.eps;
     const int row = blockIdx.x;
-    // 16-byte chunk c (elements 8c .. 8c+7) of row `row` of g
-    auto gdst = [&](int c) -> uint16_t * {
-        return a.packed ? g + gemm_pack_index(row, (int64_t)c << 3, H >> 6) : g + (int64_t)row * H + (c << 3);
-    };
-    if (row >= a.n_rows) {
-        // padding rows of the packed layout
-        for (int c = threadIdx.x; c < (H >> 3); c += blockDim.x) *(u32x4 *)gdst(c) = u32x4{0u, 0u, 0u, 0u};
-        return;
-    }
     uint16_t *x = a.f + (int64_t)row * H;
     __shared__ float red[4];
     float ss = 0.f;
@@ -80,17 +70,120 @@ __global__ __launch_bounds__(256) void k_hidden_norm(const HiddenNormArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             o[q] = pack2(bf_lo(wv[q]) * (bf_lo(v[q]) * rinv), bf_hi(wv[q]) * (bf_hi(v[q]) * rinv));
-        *(u32x4 *)gdst(c) = o;
+        *(u32x4 *)(g + (int64_t)row * H + (c << 3)) = o;
     }
+}
+
+// hidden_norm into the packed token order, R rows (1, 2 or 4) per workgroup: the R rows'
+// f (summed from the partials and rounded, or as given) is staged in LDS while each row's sum of
+// squares is taken, then every 16-byte piece of g goes out in packed order, where the R rows'
+// pieces of one (stage, slice, lane half) are R*16 bytes in a row.  Rows past n_rows (up to the
+// next multiple of 64) come out zero.  f is not written back.
+constexpr int kHnpThreads = 512;
+constexpr int kHnpLds = 128 * 1024;   // the larger of the two LDS sizes (R * H * 2 bytes fit in it)
+
+template <int LDS>
+__global__ __launch_bounds__(kHnpThreads) void k_hidden_norm_packed(const HiddenNormArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t hn_lds[LDS];
+    uint16_t *rows = (uint16_t *)hn_lds;                // [R][H] bf16
+    __shared__ float ssp[8], rinv_s[32];
+    const int R = a.packed;                             // rows per workgroup
+    const int H = a.H, cpr = H >> 3;                    // 16-byte chunks per row
+    const int n0 = blockIdx.x * R;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // phase 1: wpr waves per row (R < 8) or R/8 rows per wave (R >= 8)
+    const int wpr = R < 8 ? 8 / R : 1;
+    const int rpw = R < 8 ? 1 : R / 8;
+    for (int i = 0; i < rpw; ++i) {
+        const int r = R < 8 ? wave / wpr : wave + 8 * i;
+        const int part = R < 8 ? wave % wpr : 0;
+        const int n = n0 + r;
+        float ss = 0.f;
+        for (int c = part * 64 + lane; c < cpr; c += 64 * wpr) {
+            u32x4 v = u32x4{0u, 0u, 0u, 0u};
+            if (n < a.n_rows) {
+                if (a.part) {
+                    float s8[8];
+                    const float *src = a.part + (int64_t)n * H + (c << 3);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s8[e] = 0.f;
+                    for (int sp = 0; sp < a.S; ++sp) {
+                        const float4 lo = *(const float4 *)(src + (int64_t)sp * a.n_rows * H);
+                        const float4 hi = *(const float4 *)(src + (int64_t)sp * a.n_rows * H + 4);
+                        s8[0] += lo.x; s8[1] += lo.y; s8[2] += lo.z; s8[3] += lo.w;
+                        s8[4] += hi.x; s8[5] += hi.y; s8[6] += hi.z; s8[7] += hi.w;
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) v[q] = pack2(s8[2 * q], s8[2 * q + 1]);
+                } else {
+                    v = *(const u32x4 *)(a.f + (int64_t)n * H + (c << 3));
+                }
+            }
+            *(u32x4 *)(rows + (int64_t)r * H + (c << 3)) = v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float x = bf_lo(v[q]), y = bf_hi(v[q]);
+                ss += x * x + y * y;
+            }
+        }
+        ss = wave_sum(ss);
+        if (R < 8) {
+            if (lane == 0) ssp[wave] = ss;
+        } else if (lane == 0) {
+            rinv_s[r] = 1.0f / sqrtf(ss / (float)H + a.eps);
+        }
+    }
+    __syncthreads();
+    if (R < 8 && tid < R) {
+        float ss = 0.f;
+        for (int q = 0; q < wpr; ++q) ss += ssp[tid * wpr + q];
+        rinv_s[tid] = 1.0f / sqrtf(ss / (float)H + a.eps);
+    }
+    __syncthreads();
+    // phase 2: piece p = (q, r), q = (it*4 + s)*2 + fh in memory order, r the row in the group
+    const int iters = H >> 6;
+    const int64_t b = n0 >> 6, j = (n0 >> 5) & 1, fr0 = n0 & 31;
+    for (int p = tid; p < R * cpr; p += kHnpThreads) {
+        const int r = p % R, q = p / R;
+        const int fh = q & 1, sl = (q >> 1) & 3, it = q >> 3;
+        const int k = 64 * it + 32 * fh + 8 * sl;
+        const u32x4 v = *(const u32x4 *)(rows + (int64_t)r * H + k);
+        const u32x4 wv = *(const u32x4 *)(a.w + k);
+        const float ri = rinv_s[r];
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            o[e] = pack2(bf_lo(wv[e]) * (bf_lo(v[e]) * ri), bf_hi(wv[e]) * (bf_hi(v[e]) * ri));
+        const int64_t dst = ((((b * iters + it) * 4 + sl) * 2 + j) * 64 + fr0 + r + 32 * fh) * 8;
+        *(u32x4 *)(a.g + dst) = o;
+    }
+}
+
+// Rows per workgroup of the packed variant: 4 or 2 when their rows fit 32 KB of LDS (several
+// workgroups per CU, so that some read while others write: measured at 4096 x 4096, R = 4 takes
+// 15.5 us, R = 1 32 us) and the padded rows still give at least 256 workgroups, else 1.
+int hidden_norm_rows(int n_rows, int H) {
+    const int Mp = (n_rows + 63) / 64 * 64;
+    for (int R = 4; R > 1; R >>= 1)
+        if ((int64_t)R * H * 2 <= kHnpLds / 4 && Mp / R >= 256) return R;
+    return 1;
 }
 
 hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint16_t *w, uint16_t *g, int n_rows,
                               int H, float eps, bool packed, hipStream_t s) {
     if (n_rows == 0) return hipSuccess;
     if (H % (packed ? 64 : 8) != 0 || (part && S < 1)) return hipErrorInvalidValue;
-    const int grid = packed ? (n_rows + 63) / 64 * 64 : n_rows;
-    return launch1(k_hidden_norm, dim3(grid), dim3(256), s,
-                   HiddenNormArgs{w, f, g, part, S, n_rows, H, eps, packed ? 1 : 0});
+    if (!packed)
+        return launch1(k_hidden_norm, dim3(n_rows), dim3(256), s, HiddenNormArgs{w, f, g, part, S, n_rows, H, eps, 0});
+    const int R = hidden_norm_rows(n_rows, H);
+    const int64_t lds = (int64_t)R * H * 2;
+    if (lds > kHnpLds) return hipErrorInvalidValue;
+    const int Mp = (n_rows + 63) / 64 * 64;
+    const HiddenNormArgs args{w, f, g, part, S, n_rows, H, eps, R};
+    // the smallest LDS size that holds the rows (LDS per workgroup bounds workgroups per CU)
+    if (lds <= kHnpLds / 4) return launch1(k_hidden_norm_packed<kHnpLds / 4>, dim3(Mp / R), dim3(kHnpThreads), s, args);
+    if (lds <= kHnpLds / 2) return launch1(k_hidden_norm_packed<kHnpLds / 2>, dim3(Mp / R), dim3(kHnpThreads), s, args);
+    return launch1(k_hidden_norm_packed<kHnpLds>, dim3(Mp / R), dim3(kHnpThreads), s, args);
 }
 
 // ---------------------------------------------------------------------------
