@@ -86,17 +86,15 @@ template <int LDS>
 __global__ __launch_bounds__(kHnpThreads) void k_hidden_norm_packed(const HiddenNormArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t hn_lds[LDS];
     uint16_t *rows = (uint16_t *)hn_lds;                // [R][H] bf16
-    __shared__ float ssp[8], rinv_s[32];
-    const int R = a.packed;                             // rows per workgroup
+    __shared__ float ssp[8], rinv_s[4];
+    const int R = a.packed;                             // rows per workgroup: 1, 2 or 4
     const int H = a.H, cpr = H >> 3;                    // 16-byte chunks per row
     const int n0 = blockIdx.x * R;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    // phase 1: wpr waves per row (R < 8) or R/8 rows per wave (R >= 8)
-    const int wpr = R < 8 ? 8 / R : 1;
-    const int rpw = R < 8 ? 1 : R / 8;
-    for (int i = 0; i < rpw; ++i) {
-        const int r = R < 8 ? wave / wpr : wave + 8 * i;
-        const int part = R < 8 ? wave % wpr : 0;
+    // phase 1: wpr = 8 / R waves per row, each summing every wpr-th run of 64 chunks
+    const int wpr = 8 / R;
+    {
+        const int r = wave / wpr, part = wave % wpr;
         const int n = n0 + r;
         float ss = 0.f;
         for (int c = part * 64 + lane; c < cpr; c += 64 * wpr) {
@@ -127,14 +125,10 @@ __global__ __launch_bounds__(kHnpThreads) void k_hidden_norm_packed(const Hidden
             }
         }
         ss = wave_sum(ss);
-        if (R < 8) {
-            if (lane == 0) ssp[wave] = ss;
-        } else if (lane == 0) {
-            rinv_s[r] = 1.0f / sqrtf(ss / (float)H + a.eps);
-        }
+        if (lane == 0) ssp[wave] = ss;
     }
     __syncthreads();
-    if (R < 8 && tid < R) {
+    if (tid < R) {
         float ss = 0.f;
         for (int q = 0; q < wpr; ++q) ss += ssp[tid * wpr + q];
         rinv_s[tid] = 1.0f / sqrtf(ss / (float)H + a.eps);

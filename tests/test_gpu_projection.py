@@ -68,6 +68,9 @@ GQA_W1 = Geometry(kind=GQA, n_tgt=2, tgt_hidden=256, hidden=256, n_layers=5, n_k
                   rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
 GQA_W2 = Geometry(kind=GQA, n_tgt=1, tgt_hidden=384, hidden=384, n_layers=5, n_kv_heads=2, head_dim=64, latent_dim=0,
                   rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
+# k_in = 2048: the large-batch fc GEMM splits over k (2 splits) ahead of the packed hidden_norm
+GQA_W3 = Geometry(kind=GQA, n_tgt=2, tgt_hidden=1024, hidden=256, n_layers=5, n_kv_heads=1, head_dim=64, latent_dim=0,
+                  rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=4)
 MLA_G = Geometry(kind=MLA, n_tgt=2, tgt_hidden=256, hidden=512, n_layers=2, n_kv_heads=1, head_dim=0, latent_dim=512,
                  rope_dim=64, eps=1e-6, page_size=16, width=4, block_size=7)
 
@@ -85,6 +88,7 @@ PROJ_CASES = [
     ("gqa256-B30-tiled", GQA_G256, 30, RopeSpec(theta=1e4, rot=256)),
     ("gqaW640-B40", GQA_W1, 40, RopeSpec(theta=1e6, rot=64)),
     ("gqaW640-B70", GQA_W1, 70, RopeSpec(theta=1e6, rot=64)),
+    ("gqaW640-B70-splitfc", GQA_W3, 70, RopeSpec(theta=1e6, rot=64)),
     ("gqaW1280-B130", GQA_W2, 130, RopeSpec(theta=1e6, rot=64, yarn=True, factor=4.0, orig_ctx=1024.0)),
     ("mla-B1", MLA_G, 1, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
     ("mla-B3", MLA_G, 3, RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0)),
