@@ -78,24 +78,34 @@ int choose_kv_splits(int tiles, int kblocks, int64_t M) {
 // The small-batch K/V kernel's groups: S splits of the K/V GEMM, each a multiple of 8 k-blocks
 // (every wave takes the same number of blocks of every tile) whose g fits the LDS stage, times
 // groups of ntg consecutive 16-feature tiles (ntg <= the tiles of one unit, so a group touches at
-// most two units).  Picks the largest group count that fits the resident workgroup slots (one wave
-// of groups, all of equal size), preferring fewer splits on ties.  False when no split qualifies.
+// most two units).  Among the choices that fit the resident workgroup slots (one wave of groups,
+// all of equal size) it takes the one with the least work on the busiest CU, preferring more
+// groups, then fewer splits, on ties.  False when no split qualifies.
 bool choose_kv_groups(const dfkv_geom *g, int64_t M, int *S_out, int *ntg_out) {
     const int kb = g->hidden / 128;
     const int T = (int)(out_dim(g) / 16);
     const int tpu = (g->kind == DFKV_GQA ? g->head_dim : per_layer(g)) / 16;
+    // The groups are dealt one per CU per round (two resident per CU), so the busiest CU streams
+    // ceil(n / CUs) groups of ntg tiles x kb/S k-blocks: minimise that, ties to more groups.
+    const int cus = kKvSlots / 2;
     int best_n = 0, best_S = 0, best_ntg = 0;
+    int64_t best_cost = 0;
     for (int S = 1; S <= kb; ++S) {
         if (kb % S || (kb / S) % 8 || !stage_fits(M, kb / S)) continue;
         for (int ntg = 1; ntg <= tpu && ntg <= T; ++ntg) {
             if (T % ntg) continue;
             const int n = S * (T / ntg);
-            const bool better = best_n == 0 ? true
-                                : (n <= kKvSlots ? (best_n > kKvSlots || n > best_n) : (best_n > kKvSlots && n < best_n));
+            const int64_t cost = (int64_t)((n + cus - 1) / cus) * ntg * (kb / S);
+            bool better;
+            if (best_n == 0) better = true;
+            else if ((n <= kKvSlots) != (best_n <= kKvSlots)) better = n <= kKvSlots;
+            else if (n > kKvSlots) better = n < best_n;
+            else better = cost < best_cost || (cost == best_cost && n > best_n);
             if (better) {
                 best_n = n;
                 best_S = S;
                 best_ntg = ntg;
+                best_cost = cost;
             }
         }
     }

@@ -190,19 +190,52 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
     }
 }
 
-// GQA with k_norm + RoPE, vectorised: one workgroup per token row; thread t takes the row's 16-byte
-// chunks t, t + 512, t + 1024 (K chunks of every layer first, then the V chunks), all loaded before
-// any is used.  A K head of hd elements is hd/8 consecutive lanes of one wave: its sum of squares
+// GQA with k_norm + RoPE, vectorised: one workgroup of 256 threads per token row; thread t takes
+// the row's 16-byte chunks t, t + 256, ..., t + 1024 (K chunks of every layer first, then the V
+// chunks).  The row's chunks are loaded first, before anything they wait on: the row's cos/sin
+// values and every layer's k_norm weights go to LDS (so no thread holds them in registers across
+// the loads, which keeps eight workgroups resident per CU), and the row's destination is looked
+// up meanwhile.  A K head of hd elements is hd/8 consecutive lanes of one wave: its sum of squares
 // is a butterfly over those lanes, and the NeoX partner of chunk q (elements j and j + hd/2) is the
 // lane hd/16 away, whose normalised values come over by lane exchange.  The per-element arithmetic
 // is that of knorm_rope_head; only the order in which the squares are summed differs.
-constexpr int kFinVThreads = 512;
-constexpr int kFinVPer = 3;
+constexpr int kFinVThreads = 256;
+constexpr int kFinVPer = 5;
+constexpr int kFinVMaxHd = 256;
 
 __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizeParams p) {
+    __shared__ __attribute__((aligned(16))) float s_cs[kFinVMaxHd];                         // cos | sin
+    __shared__ __attribute__((aligned(16))) uint16_t s_wk[DFKV_MAX_LAYERS * kFinVMaxHd];    // [L][hd]
     const int row = blockIdx.x;
     const int r = row / p.W, i = row - (row / p.W) * p.W;
     const int tid = threadIdx.x;
+
+    const int hd = p.hd, half = hd >> 1;
+    const int qh = hd >> 3, hq = qh >> 1;   // chunks per head, per half head
+    const int lch = p.nkv * qh;             // K (or V) chunks of one layer
+    const int kch = p.L * lch;              // K chunks of the row; as many V chunks follow
+    const int nch = 2 * kch;
+    auto col_of = [&](int c) -> int64_t {
+        const bool k = c < kch;
+        const int cc = k ? c : c - kch;
+        const int l = cc / lch;
+        return (int64_t)l * p.per_layer + (k ? 0 : p.nkv * hd) + (cc - l * lch) * 8;
+    };
+    u32x4 y[kFinVPer];
+    auto load_group = [&](int base) {
+#pragma unroll
+        for (int m = 0; m < kFinVPer; ++m) {
+            const int c = base + m * kFinVThreads + tid;
+            y[m] = c < nch ? load_y8(p, row, col_of(c)) : u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    load_group(0);
+
+    // the row's cos/sin values (rope_dim = hd floats) and the k_norm weights of every layer
+    const float *cs = rope_row(p.nr, row);
+    for (int c = tid; c < (hd >> 2); c += kFinVThreads) *(f32x4 *)(s_cs + 4 * c) = *(const f32x4 *)(cs + 4 * c);
+    for (int c = tid; c < p.L * qh; c += kFinVThreads)
+        *(u32x4 *)(s_wk + 8 * c) = *(const u32x4 *)(p.nr.w_knorm + 8 * (int64_t)c);
 
     if (p.advance && i == 0) request_advance(p, r);
     int64_t slot = -1;
@@ -213,45 +246,16 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
     }
     const int64_t dst0 = w ? slot_offset(p, slot) : 0;
     uint16_t *const out_row = p.kv_out ? p.kv_out + (int64_t)row * p.O : nullptr;
+    __syncthreads();
 
-    const int hd = p.hd, half = hd >> 1;
-    const int qh = hd >> 3, hq = qh >> 1;   // chunks per head, per half head
-    const int lch = p.nkv * qh;             // K (or V) chunks of one layer
-    const int kch = p.L * lch;              // K chunks of the row; as many V chunks follow
-    const int nch = 2 * kch;
-    const float *cs = rope_row(p.nr, row);
-
-    for (int base = 0; base < nch; base += kFinVThreads * kFinVPer) {
-        u32x4 y[kFinVPer], wk[kFinVPer];
-        f32x4 cv[kFinVPer][2], sv[kFinVPer][2];
-        int64_t col[kFinVPer], dst[kFinVPer];
-        uint16_t *pool[kFinVPer];
-        bool isk[kFinVPer], ok[kFinVPer];
-        // every load of this pass first
+    for (int base = 0;;) {
 #pragma unroll
         for (int m = 0; m < kFinVPer; ++m) {
             const int c = base + m * kFinVThreads + tid;
-            ok[m] = c < nch;
-            isk[m] = c < kch;
-            const int cc = !ok[m] ? 0 : isk[m] ? c : c - kch;
+            const bool ok = c < nch, isk = c < kch;
+            const int cc = !ok ? 0 : isk ? c : c - kch;
             const int l = cc / lch, rem = cc - l * lch;
             const int h = rem / qh, q = rem - h * qh;
-            col[m] = (int64_t)l * p.per_layer + (isk[m] ? 0 : p.nkv * hd) + rem * 8;
-            dst[m] = dst0 + (int64_t)h * p.sh + q * 8;
-            pool[m] = isk[m] ? p.pk[l] : p.pv[l];
-            y[m] = ok[m] ? load_y8(p, row, col[m]) : u32x4{0u, 0u, 0u, 0u};
-            wk[m] = u32x4{0u, 0u, 0u, 0u};
-            if (ok[m] && isk[m]) {
-                wk[m] = *(const u32x4 *)(p.nr.w_knorm + (int64_t)l * hd + q * 8);
-                const int j0 = (q < hq ? q : q - hq) * 8;
-                cv[m][0] = *(const f32x4 *)(cs + j0);
-                cv[m][1] = *(const f32x4 *)(cs + j0 + 4);
-                sv[m][0] = *(const f32x4 *)(cs + half + j0);
-                sv[m][1] = *(const f32x4 *)(cs + half + j0 + 4);
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < kFinVPer; ++m) {
             // sum of squares over the head's lanes (every lane takes part in the exchanges)
             float v8[8];
 #pragma unroll
@@ -265,21 +269,24 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
             for (int off = hq; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
             const float rinv = 1.0f / sqrtf(ss / (float)hd + p.nr.eps);
             // normalised values, rounded to bf16, and the partner's
+            const u32x4 wk = *(const u32x4 *)(s_wk + l * hd + q * 8);
             uint32_t u2[4], pu2[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                u2[e] = pack2(bf_lo(wk[m][e]) * (v8[2 * e] * rinv), bf_hi(wk[m][e]) * (v8[2 * e + 1] * rinv));
+                u2[e] = pack2(bf_lo(wk[e]) * (v8[2 * e] * rinv), bf_hi(wk[e]) * (v8[2 * e + 1] * rinv));
                 pu2[e] = (uint32_t)__shfl_xor((int)u2[e], hq, kWave);
             }
-            if (!ok[m]) continue;
+            if (!ok) continue;
             u32x4 o = y[m];
-            if (isk[m]) {
-                const int c = base + m * kFinVThreads + tid;
-                const bool first = ((c % qh) < hq);
+            if (isk) {
+                const bool first = q < hq;
+                const int j0 = (first ? q : q - hq) * 8;
+                const f32x4 c0 = *(const f32x4 *)(s_cs + j0), c1 = *(const f32x4 *)(s_cs + j0 + 4);
+                const f32x4 s0 = *(const f32x4 *)(s_cs + half + j0), s1 = *(const f32x4 *)(s_cs + half + j0 + 4);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float cl = cv[m][e >> 1][(2 * e) & 3], ch = cv[m][e >> 1][(2 * e + 1) & 3];
-                    const float sl = sv[m][e >> 1][(2 * e) & 3], sh = sv[m][e >> 1][(2 * e + 1) & 3];
+                    const float cl = e < 2 ? c0[2 * e] : c1[2 * e - 4], ch = e < 2 ? c0[2 * e + 1] : c1[2 * e - 3];
+                    const float sl = e < 2 ? s0[2 * e] : s1[2 * e - 4], sh = e < 2 ? s0[2 * e + 1] : s1[2 * e - 3];
                     const float ul = bf_lo(u2[e]), uh = bf_hi(u2[e]), pl = bf_lo(pu2[e]), ph = bf_hi(pu2[e]);
                     // first half: k = u c - u' s; second half: k = u c + u' s (u' the partner)
                     const float kl = first ? ul * cl - pl * sl : ul * cl + pl * sl;
@@ -287,9 +294,13 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
                     o[e] = pack2(kl, kh);
                 }
             }
-            if (out_row) *(u32x4 *)(out_row + col[m]) = o;
-            if (w) *(u32x4 *)(pool[m] + dst[m]) = o;
+            const int64_t col = (int64_t)l * p.per_layer + (isk ? 0 : p.nkv * hd) + rem * 8;
+            if (out_row) *(u32x4 *)(out_row + col) = o;
+            if (w) *(u32x4 *)((isk ? p.pk[l] : p.pv[l]) + dst0 + (int64_t)h * p.sh + q * 8) = o;
         }
+        base += kFinVThreads * kFinVPer;
+        if (base >= nch) break;
+        load_group(base);
     }
 }
 
@@ -344,7 +355,8 @@ hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s) {
     const int64_t N = (int64_t)p.B * p.W;
     if (N == 0) return hipSuccess;
     // the vectorised GQA kernel reads k_norm weights and cos/sin in 16-byte pieces
-    if (p.norm && p.kind == DFKV_GQA && ((uintptr_t)p.nr.w_knorm & 15u) == 0 && ((uintptr_t)p.nr.cos_sin & 15u) == 0)
+    if (p.norm && p.kind == DFKV_GQA && p.hd <= kFinVMaxHd && ((uintptr_t)p.nr.w_knorm & 15u) == 0 &&
+        ((uintptr_t)p.nr.cos_sin & 15u) == 0)
         return launch1(k_finalize_gqa, dim3((unsigned)N), dim3(kFinVThreads), s, p);
     return launch1(k_finalize, dim3((unsigned)N), dim3(kFinThreads), s, p);
 }
