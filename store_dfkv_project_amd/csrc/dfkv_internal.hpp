@@ -28,8 +28,12 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     u += 0x7FFFu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
+// Two fp32 -> two bf16 (lo in the low half), round to nearest, ties to even: one
+// v_cvt_pk_bf16_f32 on gfx950 (f2bf's rounding for every non-NaN input, denormals included).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
 __device__ __forceinline__ float wave_sum(float v) {

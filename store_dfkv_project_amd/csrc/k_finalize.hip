@@ -194,46 +194,61 @@ __global__ __launch_bounds__(kFinThreads) void k_finalize(const FinalizeParams p
 // the row's 16-byte chunks t, t + 256, ..., t + 1024 (K chunks of every layer first, then the V
 // chunks).  The row's chunks are loaded first, before anything they wait on: the row's cos/sin
 // values and every layer's k_norm weights go to LDS (so no thread holds them in registers across
-// the loads, which keeps eight workgroups resident per CU), and the row's destination is looked
-// up meanwhile.  A K head of hd elements is hd/8 consecutive lanes of one wave: its sum of squares
-// is a butterfly over those lanes, and the NeoX partner of chunk q (elements j and j + hd/2) is the
-// lane hd/16 away, whose normalised values come over by lane exchange.  The per-element arithmetic
-// is that of knorm_rope_head; only the order in which the squares are summed differs.
+// the loads, which keeps seven workgroups resident per CU), and the row's destination is looked
+// up meanwhile.  A K head of HD elements is HD/8 consecutive lanes of one wave: its sum of squares
+// is a butterfly over those lanes, and the NeoX partner of chunk q (elements j and j + HD/2) is the
+// lane HD/16 away, whose normalised values come over by lane exchange.  A wave whose chunks are
+// all V (or past the row) only copies.  The per-element arithmetic is that of knorm_rope_head;
+// only the order in which the squares are summed differs.
 constexpr int kFinVThreads = 256;
 constexpr int kFinVPer = 5;
-constexpr int kFinVMaxHd = 256;
 
+template <int HD>
 __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizeParams p) {
-    __shared__ __attribute__((aligned(16))) float s_cs[kFinVMaxHd];                         // cos | sin
-    __shared__ __attribute__((aligned(16))) uint16_t s_wk[DFKV_MAX_LAYERS * kFinVMaxHd];    // [L][hd]
+    constexpr int half = HD / 2;
+    constexpr int qh = HD / 8, hq = qh / 2;   // chunks per head, per half head
+    // cos | sin | -sin of the row's position: a first-half chunk rotates with -sin, a second-half
+    // chunk with +sin (k = u c + u' s', u' the partner's normalised value)
+    __shared__ __attribute__((aligned(16))) float s_cs[HD + half];
+    __shared__ __attribute__((aligned(16))) uint16_t s_wk[DFKV_MAX_LAYERS * HD];      // [L][HD]
     const int row = blockIdx.x;
     const int r = row / p.W, i = row - (row / p.W) * p.W;
     const int tid = threadIdx.x;
 
-    const int hd = p.hd, half = hd >> 1;
-    const int qh = hd >> 3, hq = qh >> 1;   // chunks per head, per half head
     const int lch = p.nkv * qh;             // K (or V) chunks of one layer
     const int kch = p.L * lch;              // K chunks of the row; as many V chunks follow
     const int nch = 2 * kch;
-    auto col_of = [&](int c) -> int64_t {
-        const bool k = c < kch;
-        const int cc = k ? c : c - kch;
-        const int l = cc / lch;
-        return (int64_t)l * p.per_layer + (k ? 0 : p.nkv * hd) + (cc - l * lch) * 8;
+    // chunk c -> (K or V, layer l, offset rem in the layer's K or V part); cc / lch by a float
+    // reciprocal: cc / lch <= 2 * layers <= 64, so the product is within 4e-6 of the quotient while
+    // cc + 0.5 keeps it at least 0.5 / lch from an integer
+    const float inv_lch = 1.0f / (float)lch;
+    auto split = [&](int c, bool &isk, int &l, int &rem) {
+        isk = c < kch;
+        const int cc = isk ? c : c - kch;
+        l = (int)(((float)cc + 0.5f) * inv_lch);
+        rem = cc - l * lch;
     };
     u32x4 y[kFinVPer];
     auto load_group = [&](int base) {
 #pragma unroll
         for (int m = 0; m < kFinVPer; ++m) {
             const int c = base + m * kFinVThreads + tid;
-            y[m] = c < nch ? load_y8(p, row, col_of(c)) : u32x4{0u, 0u, 0u, 0u};
+            bool isk;
+            int l, rem;
+            split(c, isk, l, rem);
+            y[m] = c < nch ? load_y8(p, row, (int64_t)l * p.per_layer + (isk ? 0 : p.nkv * HD) + rem * 8)
+                           : u32x4{0u, 0u, 0u, 0u};
         }
     };
     load_group(0);
 
-    // the row's cos/sin values (rope_dim = hd floats) and the k_norm weights of every layer
+    // the row's cos/sin values (rope_dim = HD floats) and the k_norm weights of every layer
     const float *cs = rope_row(p.nr, row);
-    for (int c = tid; c < (hd >> 2); c += kFinVThreads) *(f32x4 *)(s_cs + 4 * c) = *(const f32x4 *)(cs + 4 * c);
+    for (int c = tid; c < HD / 4; c += kFinVThreads) {
+        const f32x4 v = *(const f32x4 *)(cs + 4 * c);
+        *(f32x4 *)(s_cs + 4 * c) = v;
+        if (c >= HD / 8) *(f32x4 *)(s_cs + half + 4 * c) = -v;
+    }
     for (int c = tid; c < p.L * qh; c += kFinVThreads)
         *(u32x4 *)(s_wk + 8 * c) = *(const u32x4 *)(p.nr.w_knorm + 8 * (int64_t)c);
 
@@ -246,55 +261,58 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
     }
     const int64_t dst0 = w ? slot_offset(p, slot) : 0;
     uint16_t *const out_row = p.kv_out ? p.kv_out + (int64_t)row * p.O : nullptr;
+    const float inv_hd = 1.0f / (float)HD;   // exact: HD is a power of two
     __syncthreads();
 
     for (int base = 0;;) {
 #pragma unroll
         for (int m = 0; m < kFinVPer; ++m) {
             const int c = base + m * kFinVThreads + tid;
-            const bool ok = c < nch, isk = c < kch;
-            const int cc = !ok ? 0 : isk ? c : c - kch;
-            const int l = cc / lch, rem = cc - l * lch;
-            const int h = rem / qh, q = rem - h * qh;
-            // sum of squares over the head's lanes (every lane takes part in the exchanges)
-            float v8[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                v8[2 * e] = bf_lo(y[m][e]);
-                v8[2 * e + 1] = bf_hi(y[m][e]);
-            }
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss += v8[e] * v8[e];
-            for (int off = hq; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
-            const float rinv = 1.0f / sqrtf(ss / (float)hd + p.nr.eps);
-            // normalised values, rounded to bf16, and the partner's
-            const u32x4 wk = *(const u32x4 *)(s_wk + l * hd + q * 8);
-            uint32_t u2[4], pu2[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                u2[e] = pack2(bf_lo(wk[e]) * (v8[2 * e] * rinv), bf_hi(wk[e]) * (v8[2 * e + 1] * rinv));
-                pu2[e] = (uint32_t)__shfl_xor((int)u2[e], hq, kWave);
-            }
-            if (!ok) continue;
+            const bool ok = c < nch;
+            bool isk;
+            int l, rem;
+            split(c, isk, l, rem);
+            const int h = rem / qh, q = rem % qh;
             u32x4 o = y[m];
-            if (isk) {
-                const bool first = q < hq;
-                const int j0 = (first ? q : q - hq) * 8;
-                const f32x4 c0 = *(const f32x4 *)(s_cs + j0), c1 = *(const f32x4 *)(s_cs + j0 + 4);
-                const f32x4 s0 = *(const f32x4 *)(s_cs + half + j0), s1 = *(const f32x4 *)(s_cs + half + j0 + 4);
+            // wave-uniform: does this wave hold any K chunk?
+            if (base + m * kFinVThreads + (tid & ~(kWave - 1)) < kch) {
+                // sum of squares over the head's lanes (every lane takes part in the exchanges)
+                float v8[8];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float cl = e < 2 ? c0[2 * e] : c1[2 * e - 4], ch = e < 2 ? c0[2 * e + 1] : c1[2 * e - 3];
-                    const float sl = e < 2 ? s0[2 * e] : s1[2 * e - 4], sh = e < 2 ? s0[2 * e + 1] : s1[2 * e - 3];
-                    const float ul = bf_lo(u2[e]), uh = bf_hi(u2[e]), pl = bf_lo(pu2[e]), ph = bf_hi(pu2[e]);
-                    // first half: k = u c - u' s; second half: k = u c + u' s (u' the partner)
-                    const float kl = first ? ul * cl - pl * sl : ul * cl + pl * sl;
-                    const float kh = first ? uh * ch - ph * sh : uh * ch + ph * sh;
-                    o[e] = pack2(kl, kh);
+                    v8[2 * e] = bf_lo(y[m][e]);
+                    v8[2 * e + 1] = bf_hi(y[m][e]);
+                }
+                float ss = 0.f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ss += v8[e] * v8[e];
+#pragma unroll
+                for (int off = hq; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+                const float rinv = __builtin_amdgcn_rsqf(ss * inv_hd + p.nr.eps);
+                // normalised values, rounded to bf16, and the partner's
+                const u32x4 wk = *(const u32x4 *)(s_wk + l * HD + q * 8);
+                uint32_t u2[4], pu2[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    u2[e] = pack2(bf_lo(wk[e]) * (v8[2 * e] * rinv), bf_hi(wk[e]) * (v8[2 * e + 1] * rinv));
+                    pu2[e] = (uint32_t)__shfl_xor((int)u2[e], hq, kWave);
+                }
+                if (isk) {
+                    const bool first = q < hq;
+                    const int j0 = (first ? q : q - hq) * 8;
+                    const float *cp = s_cs + j0, *sp = s_cs + (first ? HD : half) + j0;
+                    const f32x4 c0 = *(const f32x4 *)cp, c1 = *(const f32x4 *)(cp + 4);
+                    const f32x4 s0 = *(const f32x4 *)sp, s1 = *(const f32x4 *)(sp + 4);
+                    const float cv[8] = {c0[0], c0[1], c0[2], c0[3], c1[0], c1[1], c1[2], c1[3]};
+                    const float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        o[e] = pack2(bf_lo(u2[e]) * cv[2 * e] + bf_lo(pu2[e]) * sv[2 * e],
+                                     bf_hi(u2[e]) * cv[2 * e + 1] + bf_hi(pu2[e]) * sv[2 * e + 1]);
                 }
             }
-            const int64_t col = (int64_t)l * p.per_layer + (isk ? 0 : p.nkv * hd) + rem * 8;
+            if (!ok) continue;
+            const int64_t col = (int64_t)l * p.per_layer + (isk ? 0 : p.nkv * HD) + rem * 8;
             if (out_row) *(u32x4 *)(out_row + col) = o;
             if (w) *(u32x4 *)((isk ? p.pk[l] : p.pv[l]) + dst0 + (int64_t)h * p.sh + q * 8) = o;
         }
@@ -355,9 +373,11 @@ hipError_t launch_finalize(const FinalizeParams &p, hipStream_t s) {
     const int64_t N = (int64_t)p.B * p.W;
     if (N == 0) return hipSuccess;
     // the vectorised GQA kernel reads k_norm weights and cos/sin in 16-byte pieces
-    if (p.norm && p.kind == DFKV_GQA && p.hd <= kFinVMaxHd && ((uintptr_t)p.nr.w_knorm & 15u) == 0 &&
-        ((uintptr_t)p.nr.cos_sin & 15u) == 0)
-        return launch1(k_finalize_gqa, dim3((unsigned)N), dim3(kFinVThreads), s, p);
+    if (p.norm && p.kind == DFKV_GQA && ((uintptr_t)p.nr.w_knorm & 15u) == 0 && ((uintptr_t)p.nr.cos_sin & 15u) == 0) {
+        if (p.hd == 64) return launch1(k_finalize_gqa<64>, dim3((unsigned)N), dim3(kFinVThreads), s, p);
+        if (p.hd == 128) return launch1(k_finalize_gqa<128>, dim3((unsigned)N), dim3(kFinVThreads), s, p);
+        if (p.hd == 256) return launch1(k_finalize_gqa<256>, dim3((unsigned)N), dim3(kFinVThreads), s, p);
+    }
     return launch1(k_finalize, dim3((unsigned)N), dim3(kFinThreads), s, p);
 }
 
