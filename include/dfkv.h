@@ -113,13 +113,20 @@ typedef struct dfkv_geom {
  *          size, 16-byte aligned): above 64 rows the fc GEMM then reads it
  *          instead of w_fc, with the same result bit for bit (only the order of
  *          its bytes in memory differs).  w_fc itself is still required: at
- *          64 rows or fewer the fc streams w_fc. */
+ *          64 rows or fewer the fc streams w_fc (or w_fc_stream).
+ *  w_fc_stream, w_kv_stream  NULL, or the copies of w_fc and w_kv that
+ *          dfkv_pack_stream_weight wrote (same sizes, 16-byte aligned): at 64
+ *          rows or fewer the weight-streaming GEMMs then read them instead of
+ *          w_fc and w_kv, with the same result bit for bit.  Either may be given
+ *          without the other. */
 typedef struct dfkv_weights {
     const void *w_fc;
     const void *w_hnorm;
     const void *w_kv;
     const void *w_knorm;
     const void *w_fc_packed;
+    const void *w_fc_stream;
+    const void *w_kv_stream;
 } dfkv_weights;
 
 /* Request state of one step (all device arrays).
@@ -262,6 +269,26 @@ dfkv_status dfkv_rope_cache_build(const dfkv_rope *rope, float *cos_sin, int32_t
  * Errors: NULL; SHAPE (geometry); LAYOUT (alignment); ALIAS; HIP. */
 dfkv_status dfkv_pack_fc_weight(const dfkv_geom *g, const void *w_fc, void *w_fc_packed, dfkv_stream_t stream);
 
+/* Write a weight w (bf16 [rows][cols] row-major, 16-byte aligned: w_fc with
+ * rows = hidden, cols = n_tgt*tgt_hidden, or w_kv with rows = n_layers*per_layer,
+ * cols = hidden) in the order the weight-streaming GEMMs of <= 64 rows read it:
+ * element (o, k) goes to bf16 index
+ *   ((k/128) * (rows/16) + o/16) * 2048 + ((k%128)/32 * 64 + (k%32)/8 * 16 + o%16) * 8 + k%8.
+ * A block of 16 rows x 128 columns is 4 KB in a row, the blocks of one column
+ * range sit next to each other for all row groups, and each 1 KB of a block is
+ * what the 64 lanes of a wave load in one instruction: every workgroup of the
+ * GEMM, which owns 16 rows, then reads whole 1 KB runs, and the workgroups
+ * together sweep the weight front to back.  Done once per weight (weights are
+ * static); put the result in dfkv_weights.w_fc_stream or w_kv_stream.  A memory
+ * layout of this library, not an operation of the method: the GEMMs'
+ * arithmetic is unchanged.
+ *  rows: a positive multiple of 16; cols: a positive multiple of 128.
+ *  w_stream: device memory of rows*cols*2 bytes, 16-byte aligned; must not
+ *            overlap w.
+ * Errors: NULL; SHAPE (rows or cols); LAYOUT (alignment); ALIAS; HIP. */
+dfkv_status dfkv_pack_stream_weight(int64_t rows, int64_t cols, const void *w, void *w_stream,
+                                    dfkv_stream_t stream);
+
 /* Context projection of all N = n_reqs*W rows ([P20550]
  * TLLM_DFLASH_OVERLAP_CONTEXT_PROJECTION: fc + hidden_norm + latent GEMM +
  * RMSNorm/RoPE; [P13995] one GEMM stacked across drafter layers).
@@ -289,7 +316,7 @@ dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *
  * workspace).
  * dfkv_project_fc: f = bf16(hidden . w_fc^T) and what hidden_norm needs of it
  *   (its row statistics and w_hnorm-weighted copy, or the normalised rows) into
- *   ws.  Reads hidden, w_fc (or w_fc_packed) and w_hnorm only.
+ *   ws.  Reads hidden, w_fc (or w_fc_packed / w_fc_stream) and w_hnorm only.
  * dfkv_project_kv: from what dfkv_project_fc left in ws (same geometry and
  *   n_reqs): hidden_norm, the stacked GEMM and, with DFKV_FUSE_NORM_ROPE,
  *   k_norm + RoPE into kv_out.

@@ -197,6 +197,21 @@ NormRopeGeom nr_geom(const dfkv_geom *g, const void *w_knorm, const int32_t *ctx
 
 // ----- validation shared by the entry points --------------------------------
 
+// The tiled weight copies a call reads (dfkv_pack_stream_weight): 16-byte aligned (LAYOUT), and not
+// inside kv_out or the workspace (ALIAS).  `alias` false checks the alignment only.
+dfkv_status check_stream_weights(const dfkv_geom *g, const dfkv_weights *w, bool fc, bool kv, bool alias,
+                                 const void *kv_out, size_t kv_bytes, const void *ws, size_t ws_bytes) {
+    const void *p[2] = {fc ? w->w_fc_stream : nullptr, kv ? w->w_kv_stream : nullptr};
+    const size_t n[2] = {(size_t)g->hidden * k_in(g) * 2, (size_t)out_dim(g) * g->hidden * 2};
+    for (int i = 0; i < 2; ++i) {
+        if (!p[i]) continue;
+        if (!alias && !al16(p[i])) return DFKV_ERR_LAYOUT;
+        if (alias && (overlap(kv_out, kv_bytes, p[i], n[i]) || overlap(ws, ws_bytes, p[i], n[i])))
+            return DFKV_ERR_ALIAS;
+    }
+    return DFKV_OK;
+}
+
 dfkv_status check_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden, int64_t ld,
                           int32_t n_reqs, const int32_t *ctx, const float *cs, int32_t cache_len, void *kv_out,
                           uint32_t flags, void *ws, size_t ws_bytes, Plan *pl) {
@@ -215,11 +230,13 @@ dfkv_status check_project(const dfkv_geom *g, const dfkv_weights *w, const void 
         return DFKV_ERR_LAYOUT;
     if (fuse && (!al4(cs) || ((uintptr_t)w->w_knorm & 1u))) return DFKV_ERR_LAYOUT;
     if (w->w_fc_packed && !al16(w->w_fc_packed)) return DFKV_ERR_LAYOUT;
+    if ((st = check_stream_weights(g, w, true, true, false, nullptr, 0, nullptr, 0)) != DFKV_OK) return st;
     if (ws_bytes < pl->total) return DFKV_ERR_WORKSPACE;
     const size_t kv_bytes = (size_t)M * O * 2;
     if (w->w_fc_packed && (overlap(kv_out, kv_bytes, w->w_fc_packed, (size_t)H * K * 2) ||
                            overlap(ws, ws_bytes, w->w_fc_packed, (size_t)H * K * 2)))
         return DFKV_ERR_ALIAS;
+    if ((st = check_stream_weights(g, w, true, true, true, kv_out, kv_bytes, ws, ws_bytes)) != DFKV_OK) return st;
     const size_t hid_bytes = (size_t)((M - 1) * ld + K) * 2;
     if (overlap(kv_out, kv_bytes, hidden, hid_bytes) || overlap(kv_out, kv_bytes, ws, ws_bytes) ||
         overlap(kv_out, kv_bytes, w->w_fc, (size_t)H * K * 2) || overlap(kv_out, kv_bytes, w->w_kv, (size_t)O * H * 2) ||
@@ -430,7 +447,8 @@ dfkv_status run_fc(const dfkv_geom *g, const dfkv_weights *w, const void *hidden
     if (pl.skinny) {
         StreamParams p;
         memset(&p, 0, sizeof p);
-        p.w = (const uint16_t *)w->w_fc;
+        p.w = (const uint16_t *)(w->w_fc_stream ? w->w_fc_stream : w->w_fc);
+        p.w_tiled = w->w_fc_stream ? 1 : 0;
         p.x = (const uint16_t *)hidden;
         p.ldx = ld;
         p.M = (int32_t)pl.M;
@@ -474,7 +492,8 @@ dfkv_status run_kv(const dfkv_geom *g, const dfkv_weights *w, const int32_t *ctx
     if (pl.skinny) {
         StreamParams p;
         memset(&p, 0, sizeof p);
-        p.w = (const uint16_t *)w->w_kv;
+        p.w = (const uint16_t *)(w->w_kv_stream ? w->w_kv_stream : w->w_kv);
+        p.w_tiled = w->w_kv_stream ? 1 : 0;
         p.ldx = H;
         p.M = (int32_t)pl.M;
         p.K = (int32_t)H;
@@ -517,7 +536,8 @@ dfkv_status run_kvfin(const dfkv_geom *g, const dfkv_weights *w, const int32_t *
     const int64_t H = g->hidden, O = out_dim(g);
     KvParams kp;
     memset(&kp, 0, sizeof kp);
-    kp.kv.w = (const uint16_t *)w->w_kv;
+    kp.kv.w = (const uint16_t *)(w->w_kv_stream ? w->w_kv_stream : w->w_kv);
+    kp.kv.w_tiled = w->w_kv_stream ? 1 : 0;
     kp.kv.x = (const uint16_t *)(wsb + pl.off_f);
     kp.kv.ldx = H;
     kp.kv.M = (int32_t)pl.M;
@@ -694,12 +714,14 @@ dfkv_status dfkv_project_fc(const dfkv_geom *g, const dfkv_weights *w, const voi
     if (hidden_row_stride < K || (hidden_row_stride * 2) % 16 != 0) return DFKV_ERR_LAYOUT;
     if (!al16(hidden) || !al16(w->w_fc) || !al16(ws) || !al16(w->w_hnorm)) return DFKV_ERR_LAYOUT;
     if (w->w_fc_packed && !al16(w->w_fc_packed)) return DFKV_ERR_LAYOUT;
+    if ((st = check_stream_weights(g, w, true, false, false, nullptr, 0, nullptr, 0)) != DFKV_OK) return st;
     if (ws_bytes < pl.total) return DFKV_ERR_WORKSPACE;
     const size_t hid_bytes = (size_t)((M - 1) * hidden_row_stride + K) * 2;
     if (overlap(ws, ws_bytes, hidden, hid_bytes) || overlap(ws, ws_bytes, w->w_fc, (size_t)H * K * 2) ||
         overlap(ws, ws_bytes, w->w_hnorm, (size_t)H * 2) ||
         (w->w_fc_packed && overlap(ws, ws_bytes, w->w_fc_packed, (size_t)H * K * 2)))
         return DFKV_ERR_ALIAS;
+    if ((st = check_stream_weights(g, w, true, false, true, nullptr, 0, ws, ws_bytes)) != DFKV_OK) return st;
     return run_fc(g, w, hidden, hidden_row_stride, ws, pl, (hipStream_t)stream);
 }
 
@@ -711,6 +733,16 @@ dfkv_status dfkv_pack_fc_weight(const dfkv_geom *g, const void *w_fc, void *w_fc
     const int64_t K = k_in(g), H = g->hidden;
     if (overlap(w_fc, (size_t)H * K * 2, w_fc_packed, (size_t)H * K * 2)) return DFKV_ERR_ALIAS;
     return hip_status(launch_pack_rows((const uint16_t *)w_fc, (uint16_t *)w_fc_packed, H, K, (hipStream_t)stream));
+}
+
+dfkv_status dfkv_pack_stream_weight(int64_t rows, int64_t cols, const void *w, void *w_stream, dfkv_stream_t stream) {
+    if (!w || !w_stream) return DFKV_ERR_NULL;
+    if (rows <= 0 || cols <= 0 || rows % 16 != 0 || cols % 128 != 0 || rows > (1 << 24) || cols > (1 << 24))
+        return DFKV_ERR_SHAPE;
+    if (!al16(w) || !al16(w_stream)) return DFKV_ERR_LAYOUT;
+    const size_t bytes = (size_t)rows * (size_t)cols * 2;
+    if (overlap(w, bytes, w_stream, bytes)) return DFKV_ERR_ALIAS;
+    return hip_status(launch_pack_stream((const uint16_t *)w, (uint16_t *)w_stream, rows, cols, (hipStream_t)stream));
 }
 
 dfkv_status dfkv_project_kv(const dfkv_geom *g, const dfkv_weights *w, int32_t n_reqs, const int32_t *ctx_len_in,
@@ -729,11 +761,13 @@ dfkv_status dfkv_project_kv(const dfkv_geom *g, const dfkv_weights *w, int32_t n
     const int64_t H = g->hidden, O = out_dim(g), M = pl.M;
     if (!al16(kv_out) || !al16(w->w_hnorm) || !al16(w->w_kv) || !al16(ws)) return DFKV_ERR_LAYOUT;
     if (fuse && (!al4(cos_sin) || ((uintptr_t)w->w_knorm & 1u))) return DFKV_ERR_LAYOUT;
+    if ((st = check_stream_weights(g, w, false, true, false, nullptr, 0, nullptr, 0)) != DFKV_OK) return st;
     if (ws_bytes < pl.total) return DFKV_ERR_WORKSPACE;
     const size_t kv_bytes = (size_t)M * O * 2;
     if (overlap(kv_out, kv_bytes, ws, ws_bytes) || overlap(kv_out, kv_bytes, w->w_kv, (size_t)O * H * 2) ||
         overlap(kv_out, kv_bytes, w->w_hnorm, (size_t)H * 2))
         return DFKV_ERR_ALIAS;
+    if ((st = check_stream_weights(g, w, false, true, true, kv_out, kv_bytes, ws, ws_bytes)) != DFKV_OK) return st;
     if (fuse) {
         const size_t kn = (size_t)g->n_layers * (g->kind == DFKV_GQA ? g->head_dim : g->latent_dim) * 2;
         if (overlap(kv_out, kv_bytes, cos_sin, (size_t)cache_len * g->rope_dim * 4) ||

@@ -143,6 +143,14 @@ hipError_t launch_hidden_norm(uint16_t *f, const float *part, int S, const uint1
 hipError_t launch_rope_cache(const dfkv_rope &r, float *cs, int cache_len, hipStream_t s);
 // dst = src [rows][K] (rows and K multiples of 64) in the fragment order of gemm_pack_index
 hipError_t launch_pack_rows(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t K, hipStream_t s);
+// Weight-streaming order of a [rows][cols] bf16 matrix (dfkv_pack_stream_weight): blocks of 16 rows
+// x 128 columns, column block major; inside a block, the 16-byte pieces in the order the 64 lanes of
+// a wave load them (load u of lane (q, c16) is row c16, columns (4u + q) * 8 .. + 8).
+__host__ __device__ inline int64_t stream_pack_index(int64_t o, int64_t k, int64_t rows) {
+    return ((k >> 7) * (rows >> 4) + (o >> 4)) * 2048 + ((((k & 127) >> 5) * 64 + ((k & 31) >> 3) * 16 + (o & 15)) << 3) +
+           (k & 7);
+}
+hipError_t launch_pack_stream(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t cols, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
 
 // Weight-streaming projection GEMM (M <= 64 token rows).
@@ -151,7 +159,8 @@ constexpr int kStageChunks = 4;     // 16-byte chunks of f each of 512 threads s
 // Whether a K/V split of nbs k-blocks over M rows stages g = hidden_norm(f) in LDS (<= 32 KB).
 inline bool stage_fits(int64_t M, int nbs) { return M <= 16 && M * nbs * 16 <= 512 * kStageChunks; }
 struct StreamParams {
-    const uint16_t *w;  // [O][K] weights
+    const uint16_t *w;  // [O][K] weights: row-major, or (w_tiled) in the streaming order below
+    int32_t w_tiled;    // w as dfkv_pack_stream_weight writes it
     const uint16_t *x;  // activation rows (row stride ldx): hidden for fc; f (staged) or g for the K/V GEMM
     int64_t ldx;
     int32_t M, K, O, S, nbs;  // nbs: 128-wide k-blocks per split

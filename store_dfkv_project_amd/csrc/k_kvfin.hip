@@ -268,12 +268,19 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     const int total = ntg * nbw;        // this wave's blocks over the group
 
     u32x4 a[D][4];
+    // this lane's 16-byte piece u of k-block kb of tile t0 + i: row (t0 + i)*16 + c16, columns
+    // kb*128 + (4u + q)*8 of a row-major weight; piece u*64 + q*16 + c16 of block (kb, t0 + i) of a
+    // tiled one (stream_pack_index)
+    const uint16_t *wl = p.w_tiled ? p.w + (int64_t)t0 * 2048 + (q * 16 + c16) * 8
+                                   : p.w + (int64_t)(t0 * 16 + c16) * p.K + q * 8;
+    const int64_t w_t = p.w_tiled ? 2048 : (int64_t)16 * p.K;
+    const int64_t w_kb = p.w_tiled ? (int64_t)(p.O >> 4) * 2048 : 128;
+    const int w_u = p.w_tiled ? 512 : 32;
     auto load = [&](int slot, int f) {
         const int i = f / nbw, j = f - (f / nbw) * nbw;
-        const uint16_t *wrow = p.w + (int64_t)((t0 + i) * 16 + c16) * p.K;
-        const int64_t k = (int64_t)(kb0 + wave + j * WAVES) * 128;
+        const int64_t kb = kb0 + wave + j * WAVES;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wrow + k + (u * 4 + q) * 8);
+        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wl + i * w_t + kb * w_kb + u * w_u);
     };
 #pragma unroll
     for (int d = 0; d < D; ++d)

@@ -205,6 +205,25 @@ hipError_t launch_pack_rows(const uint16_t *src, uint16_t *dst, int64_t rows, in
     return launch1(k_pack_rows, dim3((unsigned)((chunks + 255) / 256)), dim3(256), s, PackArgs{src, dst, rows, K});
 }
 
+// A row-major bf16 matrix [rows][K] rewritten in the weight-streaming order of stream_pack_index:
+// one thread per 16-byte chunk (8 consecutive k stay together), writes contiguous along threads.
+__global__ __launch_bounds__(256) void k_pack_stream(const PackArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= a.rows * (a.K >> 3)) return;
+    // t enumerates destination chunks: block (kb, ob), piece (u, q, c16)
+    const int64_t blk = t >> 8, piece = t & 255;
+    const int64_t ob = blk % (a.rows >> 4), kb = blk / (a.rows >> 4);
+    const int u = (int)(piece >> 6), q = (int)((piece >> 4) & 3), c16 = (int)(piece & 15);
+    const int64_t o = ob * 16 + c16, k = kb * 128 + (4 * u + q) * 8;
+    *(u32x4 *)(a.dst + (t << 3)) = *(const u32x4 *)(a.src + o * a.K + k);
+}
+
+hipError_t launch_pack_stream(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t K, hipStream_t s) {
+    if (rows % 16 != 0 || K % 128 != 0 || rows <= 0) return hipErrorInvalidValue;
+    const int64_t chunks = rows * (K >> 3);
+    return launch1(k_pack_stream, dim3((unsigned)((chunks + 255) / 256)), dim3(256), s, PackArgs{src, dst, rows, K});
+}
+
 // ---------------------------------------------------------------------------
 // cos/sin cache in fp64 (stored fp32).  Plain RoPE: inv_i = theta^(-2i/rot).
 // YaRN (Peng et al. 2023, "NTK-by-parts" + attention temperature, in the HF

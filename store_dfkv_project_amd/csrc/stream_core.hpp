@@ -16,6 +16,12 @@
 //    so each load instruction reads 64 contiguous bytes of each of 16 rows; the
 //    activation (B) fragment uses the same k permutation, which leaves every
 //    dot product unchanged;
+//  * with a tiled weight (dfkv_pack_stream_weight) the same pieces come from a
+//    copy in which each 16-row x 128-column block is 4 KB in a row, ordered as
+//    the lanes load it (each load instruction reads 1 KB in a row), and the
+//    blocks of one k-block sit side by side for all tiles, so the workgroups
+//    together sweep the weight front to back (measured on MI355X: the bs=1 fc
+//    stream 20.8 -> 18.4 us for 100.8 MB);
 //  * the waves of a workgroup take interleaved k-blocks; each wave keeps a ring
 //    of D k-blocks of weights (and activations) in flight;
 //  * fc reads its activations (hidden rows) through L2 in the register ring; its
@@ -44,7 +50,12 @@ __device__ __forceinline__ void stream_tile(const StreamParams &p, int t, int s,
     constexpr int NT = WAVES * 64;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
     const int M = p.M;
-    const uint16_t *wrow = p.w + (int64_t)(t * 16 + c16) * p.K;
+    // this lane's 16-byte piece u of 128-wide k-block kb: row t*16 + c16, columns kb*128 + (4u + q)*8 of
+    // a row-major weight; piece u*64 + q*16 + c16 of block (kb, t) of a tiled one (stream_pack_index)
+    const uint16_t *wl = p.w_tiled ? p.w + (int64_t)t * 2048 + (q * 16 + c16) * 8
+                                   : p.w + (int64_t)(t * 16 + c16) * p.K + q * 8;
+    const int64_t w_kb = p.w_tiled ? (int64_t)(p.O >> 4) * 2048 : 128;
+    const int w_u = p.w_tiled ? 512 : 32;
     const int kb0 = s * p.nbs;  // first k-block (128 wide) of the split
     const int kc = p.nbs * 128, ldg = kc + 8;
     const int nbw = wave < p.nbs ? (p.nbs - wave + WAVES - 1) / WAVES : 0;
@@ -52,9 +63,9 @@ __device__ __forceinline__ void stream_tile(const StreamParams &p, int t, int s,
     u32x4 a[D][4];
     u32x4 b[STAGE ? 1 : D][NG][4];
     auto load = [&](int slot, int j) {
-        const int64_t k = (int64_t)(kb0 + wave + j * WAVES) * 128;
+        const int64_t kb = kb0 + wave + j * WAVES, k = kb * 128;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wrow + k + (u * 4 + q) * 8);
+        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wl + kb * w_kb + u * w_u);
         if (!STAGE) {
 #pragma unroll
             for (int ng = 0; ng < NG; ++ng) {

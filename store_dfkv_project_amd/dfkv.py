@@ -35,7 +35,7 @@ DFKV_FUSE_NORM_ROPE = 1
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
             "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join", "dfkv_block_table_decode",
-            "dfkv_strict_accept", "dfkv_paged_store_rows", "dfkv_pack_fc_weight")
+            "dfkv_strict_accept", "dfkv_paged_store_rows", "dfkv_pack_fc_weight", "dfkv_pack_stream_weight")
 
 
 class dfkv_geom(C.Structure):
@@ -47,7 +47,7 @@ class dfkv_geom(C.Structure):
 
 class dfkv_weights(C.Structure):
     _fields_ = [("w_fc", C.c_void_p), ("w_hnorm", C.c_void_p), ("w_kv", C.c_void_p), ("w_knorm", C.c_void_p),
-                ("w_fc_packed", C.c_void_p)]
+                ("w_fc_packed", C.c_void_p), ("w_fc_stream", C.c_void_p), ("w_kv_stream", C.c_void_p)]
 
 
 class dfkv_requests(C.Structure):
@@ -110,6 +110,7 @@ def _load() -> C.CDLL:
         "dfkv_project": ([gp, wp, P, I64, I32, P, P, I32, P, U32, P, SZ, P], C.c_int),
         "dfkv_project_fc": ([gp, wp, P, I64, I32, P, SZ, P], C.c_int),
         "dfkv_pack_fc_weight": ([gp, P, P, P], C.c_int),
+        "dfkv_pack_stream_weight": ([I64, I64, P, P, P], C.c_int),
         "dfkv_project_kv": ([gp, wp, I32, P, P, I32, P, U32, P, SZ, P], C.c_int),
         "dfkv_norm_rope": ([gp, P, I32, P, P, I32, P, P], C.c_int),
         "dfkv_paged_store": ([gp, P, rp, pp, P, P, P], C.c_int),
@@ -180,8 +181,9 @@ def make_geom(**kw) -> dfkv_geom:
     return g
 
 
-def make_weights(w_fc, w_hnorm, w_kv, w_knorm, w_fc_packed=None) -> dfkv_weights:
-    return dfkv_weights(_ptr(w_fc), _ptr(w_hnorm), _ptr(w_kv), _ptr(w_knorm), _ptr(w_fc_packed))
+def make_weights(w_fc, w_hnorm, w_kv, w_knorm, w_fc_packed=None, w_fc_stream=None, w_kv_stream=None) -> dfkv_weights:
+    return dfkv_weights(_ptr(w_fc), _ptr(w_hnorm), _ptr(w_kv), _ptr(w_knorm), _ptr(w_fc_packed), _ptr(w_fc_stream),
+                        _ptr(w_kv_stream))
 
 
 def make_requests(n_reqs, ctx_len_in, n_acc, alloc_limit, is_dummy, row_valid, block_table, bt_row_stride, bt_cols,
@@ -297,6 +299,11 @@ def dfkv_project_fc(geom, weights, hidden, hidden_row_stride, n_reqs, ws, ws_byt
 def dfkv_pack_fc_weight(geom, w_fc, w_fc_packed, stream=None) -> None:
     _check(_lib.dfkv_pack_fc_weight(_ref(geom), _ptr(w_fc), _ptr(w_fc_packed), _stream(stream)),
            "dfkv_pack_fc_weight")
+
+
+def dfkv_pack_stream_weight(rows, cols, w, w_stream, stream=None) -> None:
+    _check(_lib.dfkv_pack_stream_weight(int(rows), int(cols), _ptr(w), _ptr(w_stream), _stream(stream)),
+           "dfkv_pack_stream_weight")
 
 
 def dfkv_project_kv(geom, weights, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out, flags, ws, ws_bytes,

@@ -43,11 +43,14 @@ class DeviceStep:
     [page][slot][R+P].  weight_copies > 1 keeps that many copies of the weights at distinct addresses
     (so that a timing loop can rotate through them and read them from HBM, not from the cache).
     pack_fc: also give each copy a packed fc weight (dfkv_pack_fc_weight), which the large-batch fc
-    GEMM then reads.
+    GEMM then reads.  pack_stream: also give each copy tiled fc and K/V weights
+    (dfkv_pack_stream_weight), which the weight-streaming GEMMs of <= 64 rows then read; None packs
+    them when the workload has <= 64 rows.
     """
 
     def __init__(self, wl, device: str = "cuda", pool_layout: str = "nhd", weight_copies: int = 1,
-                 pool_seed: int = 1234, with_weights: bool = True, pack_fc: bool = True):
+                 pool_seed: int = 1234, with_weights: bool = True, pack_fc: bool = True,
+                 pack_stream: Optional[bool] = None):
         self.wl = wl
         g = wl.geom
         self.geom = g
@@ -61,7 +64,10 @@ class DeviceStep:
         self.hidden = _dev(wl.hidden, device)
         self.weights = []
         self.w_fc_packed = []
+        self.w_stream = []
         self.weight_structs = []
+        if pack_stream is None:
+            pack_stream = N <= 64
         if with_weights and wl.w_fc is not None:
             base = [_dev(wl.w_fc, device), _dev(wl.w_hnorm, device), _dev(wl.w_kv, device), _dev(wl.w_knorm, device)]
             for c in range(weight_copies):
@@ -72,7 +78,14 @@ class DeviceStep:
                     pk = torch.empty_like(ws[0])
                     dfkv.dfkv_pack_fc_weight(self.gs, ws[0], pk)
                 self.w_fc_packed.append(pk)
-                self.weight_structs.append(dfkv.make_weights(*ws, w_fc_packed=pk))
+                st = (None, None)
+                if pack_stream:
+                    st = (torch.empty_like(ws[0]), torch.empty_like(ws[2]))
+                    dfkv.dfkv_pack_stream_weight(g.hidden, g.k_in, ws[0], st[0])
+                    dfkv.dfkv_pack_stream_weight(g.out_dim, g.hidden, ws[2], st[1])
+                self.w_stream.append(st)
+                self.weight_structs.append(dfkv.make_weights(*ws, w_fc_packed=pk, w_fc_stream=st[0],
+                                                             w_kv_stream=st[1]))
         # request state
         self.ctx_len = _dev(wl.ctx_len.astype(np.int32), device)
         self.n_acc = _dev(wl.n_acc.astype(np.int32), device)

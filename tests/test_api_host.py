@@ -150,6 +150,39 @@ def test_project_packed_weight_checks():
     assert status_of(dfkv.dfkv_project_fc, **dict(fc, ws_bytes=ok_ws - 256)) == dfkv.DFKV_ERR_WORKSPACE
 
 
+def test_pack_stream_weight_validation():
+    f = dfkv.dfkv_pack_stream_weight
+    assert status_of(f, 4096, 12288, None, addr(2)) == dfkv.DFKV_ERR_NULL
+    assert status_of(f, 4096, 12288, addr(1), None) == dfkv.DFKV_ERR_NULL
+    for rows, cols in ((4088, 12288), (4096, 12224), (0, 128), (16, 0), (-16, 128)):
+        assert status_of(f, rows, cols, addr(1), addr(2)) == dfkv.DFKV_ERR_SHAPE, (rows, cols)
+    assert status_of(f, 4096, 12288, addr(1) + 8, addr(2)) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(f, 4096, 12288, addr(1), addr(2) + 2) == dfkv.DFKV_ERR_LAYOUT
+    # the tiled copy over the row-major one (either way round)
+    assert status_of(f, 4096, 12288, addr(1), addr(1) + 4096) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(f, 4096, 12288, addr(1) + 4096, addr(1)) == dfkv.DFKV_ERR_ALIAS
+
+
+def test_project_stream_weight_checks():
+    ok_ws = dfkv.dfkv_workspace_size(geom(), 1)
+    w = lambda fs=None, ks=None: dfkv.make_weights(addr(1), addr(2), addr(3), addr(4), w_fc_stream=fs, w_kv_stream=ks)
+    P = dfkv.dfkv_project
+    assert status_of(P, **project_args(weights=w(fs=addr(10) + 8), ws_bytes=ok_ws)) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(P, **project_args(weights=w(ks=addr(11) + 4), ws_bytes=ok_ws)) == dfkv.DFKV_ERR_LAYOUT
+    # a tiled weight over kv_out, or inside the workspace
+    assert status_of(P, **project_args(weights=w(fs=addr(8)), ws_bytes=ok_ws)) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(P, **project_args(weights=w(ks=addr(9) + 256), ws_bytes=ok_ws)) == dfkv.DFKV_ERR_ALIAS
+    assert status_of(P, **project_args(weights=w(ks=addr(8) - 1024), ws_bytes=ok_ws)) == dfkv.DFKV_ERR_ALIAS
+    # the fc stage checks the tiled fc weight only, the K/V stage the tiled K/V weight only
+    fc = dict(geom=geom(), hidden=addr(5), hidden_row_stride=12288, n_reqs=1, ws=addr(9), ws_bytes=ok_ws, stream=0)
+    assert status_of(dfkv.dfkv_project_fc, **dict(fc, weights=w(fs=addr(10) + 2))) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(dfkv.dfkv_project_fc, **dict(fc, weights=w(fs=addr(9)))) == dfkv.DFKV_ERR_ALIAS
+    kv = dict(geom=geom(), n_reqs=1, ctx_len_in=addr(6), cos_sin=addr(7), cache_len=4096, kv_out=addr(8),
+              flags=dfkv.DFKV_FUSE_NORM_ROPE, ws=addr(9), ws_bytes=ok_ws, stream=0)
+    assert status_of(dfkv.dfkv_project_kv, **dict(kv, weights=w(ks=addr(11) + 2))) == dfkv.DFKV_ERR_LAYOUT
+    assert status_of(dfkv.dfkv_project_kv, **dict(kv, weights=w(ks=addr(8)))) == dfkv.DFKV_ERR_ALIAS
+
+
 def test_project_alias_checks():
     ok_ws = dfkv.dfkv_workspace_size(geom(), 1)
     # kv_out inside the hidden rows

@@ -235,6 +235,66 @@ def test_pack_fc_weight_layout(H, K):
     assert torch.equal(pk, want)
 
 
+@pytest.mark.parametrize("rows,cols", [(16, 128), (48, 384), (1728, 7168), (4096, 12288)])
+def test_pack_stream_weight_layout(rows, cols):
+    """dfkv_pack_stream_weight puts element (o, k) where the header's formula says: checked against the same
+    permutation written as a reshape of the [rows][cols] matrix."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(rows + cols)
+    w = torch.randint(-32768, 32768, (rows, cols), dtype=torch.int16, device="cuda", generator=gen)
+    st = torch.empty_like(w)
+    dfkv.dfkv_pack_stream_weight(rows, cols, w, st)
+    torch.cuda.synchronize()
+    # o = 16 ob + c16, k = 128 kb + 32 u + 8 q + e  ->  [kb][ob][u][q][c16][e]
+    want = w.view(rows // 16, 16, cols // 128, 4, 4, 8).permute(2, 0, 3, 4, 1, 5).reshape(rows, cols)
+    assert torch.equal(st, want)
+
+
+# row counts through every weight-streaming kernel: the staged K/V groups (<= 16 rows) and the
+# streaming GEMM with 1-4 row groups (17-64 rows)
+STREAM_CASES = [("gqa128-B1", GQA_G, 1), ("gqa128-B4", GQA_G, 4), ("gqa128-B5", GQA_G, 5), ("gqa128-B9", GQA_G, 9),
+                ("gqa128-B16", GQA_G, 16), ("gqa64-B2", GQA_G64, 2), ("gqa256-B3", GQA_G256, 3),
+                ("gqa256-B21", GQA_G256, 21), ("gqaW640-B10", GQA_W1, 10), ("mla-B1", MLA_G, 1),
+                ("mla-B3", MLA_G, 3), ("mla-B12", MLA_G, 12)]
+
+
+@pytest.mark.parametrize("name,geom,B", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_stream_weights_same_bits(orc, name, geom, B):
+    """At <= 64 rows the streaming GEMMs read the tiled fc and K/V weights when given them: the projection
+    (whole and staged) is bit for bit the one from the row-major weights, with either tiled copy alone
+    too, and matches the oracle."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    rope = RopeSpec(theta=1e6, rot=geom.rope_dim)
+    wl, ds, ref = _run_case(orc, name, geom, B, rope)
+    assert ds.N <= 64 and ds.w_stream[0][0] is not None and ds.w_stream[0][1] is not None
+    tiled_struct = ds.weight_structs[0]
+
+    def run(struct, staged=False):
+        ds.weight_structs[0] = struct
+        ds.kv_out.fill_(0x7FC0)
+        if staged:
+            ds.project_fc()
+            ds.project_kv(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+        else:
+            ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
+        torch.cuda.synchronize()
+        return ds.kv_out.clone()
+
+    tiled = run(tiled_struct)
+    assert_close_bf16(ds.bits(tiled), ref["kv"], f"{name} tiled")
+    assert torch.equal(run(tiled_struct, staged=True), tiled), "staged projection with tiled weights differs"
+    w_fc, w_hn, w_kv, w_kn = ds.weights[0]
+    fs, ks = ds.w_stream[0]
+    for label, struct in (("row-major", dfkv.make_weights(w_fc, w_hn, w_kv, w_kn)),
+                          ("tiled fc only", dfkv.make_weights(w_fc, w_hn, w_kv, w_kn, w_fc_stream=fs)),
+                          ("tiled K/V only", dfkv.make_weights(w_fc, w_hn, w_kv, w_kn, w_kv_stream=ks))):
+        assert torch.equal(run(struct), tiled), f"{label} weights give different bits"
+    ds.weight_structs[0] = tiled_struct
+
+
 PACK_CASES = [("gqa128-B30", GQA_G, 30), ("gqaW640-B70", GQA_W1, 70), ("mla-B33", MLA_G, 33), ("gqa64-B37", GQA_G64, 37)]
 
 
