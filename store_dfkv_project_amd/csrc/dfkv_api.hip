@@ -77,8 +77,7 @@ int choose_kv_splits(int tiles, int kblocks, int64_t M) {
 
 // The small-batch K/V kernel's groups: S splits of the K/V GEMM, each a multiple of 8 k-blocks
 // (every wave takes the same number of blocks of every tile) whose g fits the LDS stage, times
-// groups of ntg consecutive 16-feature tiles (ntg <= the tiles of one unit, so a group touches at
-// most two units).  Among the choices that fit the resident workgroup slots (one wave of groups,
+// groups of ntg 16-feature tiles (ntg <= the tiles of one unit).  Among the choices that fit the resident workgroup slots (one wave of groups,
 // all of equal size) it takes the one with the least work on the busiest CU, preferring more
 // groups, then fewer splits, on ties.  False when no split qualifies.
 bool choose_kv_groups(const dfkv_geom *g, int64_t M, int *S_out, int *ntg_out) {

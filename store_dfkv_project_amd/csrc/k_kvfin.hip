@@ -14,8 +14,9 @@
 // Input: f = bf16(hidden . w_fc^T) and its per-16-column sums of squares, left in
 // the workspace by the fc kernel (k_stream) that runs before these.
 //
-// k_kvgroups: S splits of the K/V GEMM's k range times groups of ntg consecutive
-// 16-feature tiles; one workgroup per (split, group), all of them resident at
+// k_kvgroups: S splits of the K/V GEMM's k range times groups of ntg 16-feature
+// tiles (interleaved: group g of G takes tiles g, g + G, ...); one workgroup per
+// (split, group), all of them resident at
 // once (the group count is chosen to fit the chip's workgroup slots), each with
 // the same amount of weights to stream.  A group stages g = hidden_norm(f) for
 // its split in LDS once, streams its tiles' weights through a ring of
@@ -245,8 +246,10 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
 // k_kvgroups: one workgroup per (split, tile group)
 // ---------------------------------------------------------------------------
 
-// Group (s, t0): split s of the K/V GEMM (k-blocks [s*nbs, (s+1)*nbs), nbs a multiple of the wave
-// count, so every wave takes nbs/8 blocks of every tile) over tiles [t0, t0 + ntg).  Same per-tile
+// Group (s, g): split s of the K/V GEMM (k-blocks [s*nbs, (s+1)*nbs), nbs a multiple of the wave
+// count, so every wave takes nbs/8 blocks of every tile) over tiles g, g + G, ..., g + (ntg-1)*G
+// (G groups per split), so that the groups of a split stream neighbouring tiles at the same time
+// (with a tiled weight, G adjacent 4 KB blocks of each k-block).  Same per-tile
 // arithmetic as the staged K/V GEMM of stream_core.hpp: waves interleave the split's blocks, their
 // sums are added in wave order.
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvWPE, 8))) void k_kvgroups(
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     const StreamParams &p = kp.kv;
     const FinalizeParams &fin = kp.fin;
     const int groups = kp.n_groups / p.S;
-    const int s = blockIdx.x / groups, t0 = (blockIdx.x - s * groups) * kp.ntg;
+    const int s = blockIdx.x / groups, t0 = blockIdx.x - s * groups;   // tiles t0 + i*groups
     const bool book = blockIdx.x == 0;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
     const int M = p.M, ntg = kp.ntg;
@@ -268,12 +271,12 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     const int total = ntg * nbw;        // this wave's blocks over the group
 
     u32x4 a[D][4];
-    // this lane's 16-byte piece u of k-block kb of tile t0 + i: row (t0 + i)*16 + c16, columns
-    // kb*128 + (4u + q)*8 of a row-major weight; piece u*64 + q*16 + c16 of block (kb, t0 + i) of a
+    // this lane's 16-byte piece u of k-block kb of tile t = t0 + i*groups: row t*16 + c16, columns
+    // kb*128 + (4u + q)*8 of a row-major weight; piece u*64 + q*16 + c16 of block (kb, t) of a
     // tiled one (stream_pack_index)
     const uint16_t *wl = p.w_tiled ? p.w + (int64_t)t0 * 2048 + (q * 16 + c16) * 8
                                    : p.w + (int64_t)(t0 * 16 + c16) * p.K + q * 8;
-    const int64_t w_t = p.w_tiled ? 2048 : (int64_t)16 * p.K;
+    const int64_t w_t = p.w_tiled ? (int64_t)groups * 2048 : (int64_t)groups * 16 * p.K;
     const int64_t w_kb = p.w_tiled ? (int64_t)(p.O >> 4) * 2048 : 128;
     const int w_u = p.w_tiled ? 512 : 32;
     auto load = [&](int slot, int f) {
@@ -403,7 +406,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
                 for (int v = 0; v < 4; ++v) rb[(wave * 16 + q * 4 + v) * NP + c16] = acc[v];
                 acc = f32x4{0.f, 0.f, 0.f, 0.f};
                 __syncthreads();
-                const int t = t0 + i;
+                const int t = t0 + i * groups;
                 for (int idx = tid; idx < 16 * M; idx += NT) {
                     const int o = idx & 15, n = idx >> 4;
                     float y = 0.f;
