@@ -28,7 +28,7 @@
 // k_kvfinal: one workgroup per unit -- a GQA K or V head, or an MLA layer's
 // latent + rope -- and block of rows: one round of loads (the unit's split partials, its k_norm
 // weights, the rows' cos/sin values and slots), then the per-head arithmetic of
-// finalize_common.hpp into kv_out and the pools; workgroup 0 also writes the
+// finalize_common.hpp into kv_out and the pools; one more workgroup writes the
 // bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
 // inside the GEMM kernel by the last arriving group: there every dependent hop
 // (store drain, arrival atomic, partial loads) waited behind the weight stream.
@@ -60,6 +60,35 @@ __device__ __forceinline__ float *book_cs(void *b) { return (float *)((char *)b 
 // k_kvfinal: one workgroup per unit
 // ---------------------------------------------------------------------------
 
+// The bookkeeping outputs from what k_kvgroups' group 0 left in the workspace (slot, write mask,
+// context positions; bonus, embedding ids, query positions, advanced ctx_len, seq_len): one hop of
+// loads, then the stores.  A workgroup of its own, so that this hop runs beside the units' work
+// instead of after it.
+__device__ __forceinline__ void kvfinal_bookkeeping(const FinalizeParams &p, void *book) {
+    const int tid = threadIdx.x, Mall = p.M;
+    if (p.store && tid < Mall) {
+        const int64_t slot = book_slot(book)[tid];
+        p.slot[tid] = slot;
+        p.wmask[tid] = slot >= 0 ? 1 : 0;
+    }
+    if (!p.advance) return;
+    const int32_t *ctx = book_ctx(book), *ctx_new = book_ctx_new(book), *bonus = book_bonus(book);
+    for (int e = tid; e < Mall; e += kKvThreads) {
+        const int r = e / p.W, i = e - (e / p.W) * p.W;
+        p.c_pos[e] = (int32_t)((int64_t)ctx[r] + i);
+    }
+    for (int e = tid; e < p.B * p.bs_blk; e += kKvThreads) {
+        const int r = e / p.bs_blk, j = e - (e / p.bs_blk) * p.bs_blk;
+        p.emb[e] = j == 0 ? bonus[r] : p.mask_id;
+        p.q_pos[e] = ctx_new[r] + j;
+    }
+    if (tid < p.B) {
+        p.bonus[tid] = bonus[tid];
+        p.ctx_out[tid] = ctx_new[tid];
+        p.seq_len[tid] = ctx_new[tid] + p.bs_blk;
+    }
+}
+
 // Unit u (a GQA K or V head: columns [u*hd, (u+1)*hd); an MLA layer: latent + rope) for the rows
 // [n0, n0 + rpw) -- as many rows as keep the unit's partials one round of loads.  Phase A (all
 // threads, one round of loads): the split partials summed in split order and rounded to bf16, the
@@ -69,6 +98,10 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     extern __shared__ __attribute__((aligned(16))) uint16_t sh_dyn[];
     const FinalizeParams &p = kp.fin;
     const int nrb = (p.M + kp.fin_rows - 1) / kp.fin_rows;
+    if ((int)blockIdx.x == kp.n_units * nrb) {   // the last workgroup: the bookkeeping outputs
+        kvfinal_bookkeeping(p, kp.book);
+        return;
+    }
     const int u = blockIdx.x / nrb, rb = blockIdx.x - (blockIdx.x / nrb) * nrb;
     const int n0 = rb * kp.fin_rows;
     const int M = p.M - n0 < kp.fin_rows ? p.M - n0 : kp.fin_rows;  // rows of this workgroup
@@ -216,30 +249,6 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
         }
     }
 
-    // workgroup 0: the bookkeeping outputs (slot, write mask, context positions; bonus, embedding
-    // ids, query positions, advanced ctx_len, seq_len)
-    if (blockIdx.x != 0) return;
-    if (p.store && tid < Mall) {
-        const int64_t slot = book_slot(book)[tid];
-        p.slot[tid] = slot;
-        p.wmask[tid] = slot >= 0 ? 1 : 0;
-    }
-    if (!p.advance) return;
-    const int32_t *ctx = book_ctx(book), *ctx_new = book_ctx_new(book), *bonus = book_bonus(book);
-    for (int e = tid; e < Mall; e += kKvThreads) {
-        const int r = e / p.W, i = e - (e / p.W) * p.W;
-        p.c_pos[e] = (int32_t)((int64_t)ctx[r] + i);
-    }
-    for (int e = tid; e < p.B * p.bs_blk; e += kKvThreads) {
-        const int r = e / p.bs_blk, j = e - (e / p.bs_blk) * p.bs_blk;
-        p.emb[e] = j == 0 ? bonus[r] : p.mask_id;
-        p.q_pos[e] = ctx_new[r] + j;
-    }
-    if (tid < p.B) {
-        p.bonus[tid] = bonus[tid];
-        p.ctx_out[tid] = ctx_new[tid];
-        p.seq_len[tid] = ctx_new[tid] + p.bs_blk;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -465,7 +474,7 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     p.lds_cs = (int32_t)(p.lds_wk + up16((size_t)p.unit_cols * 2));
     const size_t fin_bytes = (size_t)p.lds_cs + (size_t)rows * (size_t)p.fin.nr.rope_dim * 4;
     const unsigned nrb = (unsigned)((M + rows - 1) / rows);
-    return launch1(k_kvfinal, dim3((unsigned)p.n_units * nrb), dim3(kKvThreads), s, p, fin_bytes);
+    return launch1(k_kvfinal, dim3((unsigned)p.n_units * nrb + 1), dim3(kKvThreads), s, p, fin_bytes);
 }
 
 }  // namespace dfkv
