@@ -162,93 +162,64 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     if (tid < M) sh_slot[tid] = p.store ? book_slot(book)[n0 + tid] : -1;
     __syncthreads();
 
-    // phase B
-    if (gqa) {
-        const int hd = cols, half = hd >> 1;
-        uint16_t *pool = is_v ? p.pv[l] : p.pk[l];
-        for (int n = wave; n < M; n += kKvWaves) {
-            float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                const int j = lane + q2 * 64;
-                if (j < half) {
-                    a[q2] = bf2f(y[n * hd + j]);
-                    b[q2] = bf2f(y[n * hd + j + half]);
-                }
+    // phase B: one wave per row, 16-byte chunks (lane L holds elements 8L .. 8L+7 of a head, of the
+    // latent or of the rope part); a NeoX pair's partner chunk is the lane half a head away
+    for (int n = wave; n < M; n += kKvWaves) {
+        const uint16_t *yr = y + n * cols;
+        const float *csr = cs + n * rot;
+        const int64_t slot = sh_slot[n];
+        uint16_t *out = p.kv_out ? p.kv_out + (int64_t)(n0 + n) * O + col0 : nullptr;
+        if (gqa) {
+            const int hd = cols, qh = hd >> 3;   // chunks of the head (<= 32 lanes)
+            uint16_t *d = slot >= 0 ? (is_v ? p.pv[l] : p.pk[l]) + slot_offset(p, slot) + (int64_t)h * p.sh : nullptr;
+            u32x4 v = lane < qh ? *(const u32x4 *)(yr + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+            if (norm) v = knorm_rope_chunk(v, hd, p.nr.eps, wk, csr, lane);
+            if (lane < qh) {
+                if (out) *(u32x4 *)(out + 8 * lane) = v;
+                if (d) *(u32x4 *)(d + 8 * lane) = v;
             }
-            uint16_t ka[2], kb[2];
-            if (norm) {
-                knorm_rope_head(a, b, hd, p.nr.eps, wk, cs + n * rot, lane, ka, kb);
-            } else {
-#pragma unroll
-                for (int q2 = 0; q2 < 2; ++q2) {
-                    ka[q2] = f2bf(a[q2]);
-                    kb[q2] = f2bf(b[q2]);
-                }
-            }
-            const int64_t slot = sh_slot[n];
-            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)(n0 + n) * O + col0 : nullptr;
-            uint16_t *d = slot >= 0 ? pool + slot_offset(p, slot) + (int64_t)h * p.sh : nullptr;
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                const int j = lane + q2 * 64;
-                if (j < half) {
-                    if (out) {
-                        out[j] = ka[q2];
-                        out[j + half] = kb[q2];
-                    }
-                    if (d) {
-                        d[j] = ka[q2];
-                        d[j + half] = kb[q2];
-                    }
-                }
-            }
-        }
-    } else {
-        const int R = p.nr.latent, half = rot >> 1;
-        for (int n = wave; n < M; n += kKvWaves) {
-            float v[16];
-#pragma unroll
-            for (int q2 = 0; q2 < 16; ++q2) {
-                const int e = lane + q2 * 64;
-                v[q2] = e < R ? bf2f(y[n * cols + e]) : 0.f;
-            }
-            float ra = 0.f, rb = 0.f;
-            if (lane < half) {
-                ra = bf2f(y[n * cols + R + lane]);
-                rb = bf2f(y[n * cols + R + lane + half]);
-            }
-            const int64_t slot = sh_slot[n];
-            uint16_t *out = p.kv_out ? p.kv_out + (int64_t)(n0 + n) * O + col0 : nullptr;
+        } else {
+            const int R = p.nr.latent, qr = R >> 3, qp = rot >> 3;
             uint16_t *d = slot >= 0 ? p.pk[l] + slot_offset(p, slot) : nullptr;
-            const float rinv = norm ? latent_rinv(v, R, p.nr.eps) : 1.f;
+            // latent: up to two chunks per lane (R <= 1024); rinv over all of them
+            u32x4 v[2];
+            float ss = 0.f;
 #pragma unroll
-            for (int q2 = 0; q2 < 16; ++q2) {
-                const int e = lane + q2 * 64;
-                if (e < R) {
-                    const uint16_t o = norm ? latent_elem(wk[e], v[q2], rinv) : f2bf(v[q2]);
-                    if (out) out[e] = o;
-                    if (d) d[e] = o;
+            for (int k = 0; k < 2; ++k) {
+                const int c = lane + 64 * k;
+                v[k] = c < qr ? *(const u32x4 *)(yr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) ss += bf_lo(v[k][e]) * bf_lo(v[k][e]) + bf_hi(v[k][e]) * bf_hi(v[k][e]);
+            }
+            if (norm) {
+                ss = wave_sum(ss);
+                const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / (float)R) + p.nr.eps);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int c = lane + 64 * k;
+                    if (c >= qr) continue;
+                    const u32x4 wv = *(const u32x4 *)(wk + 8 * c);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        v[k][e] = pack2(bf_lo(wv[e]) * (bf_lo(v[k][e]) * rinv), bf_hi(wv[e]) * (bf_hi(v[k][e]) * rinv));
                 }
             }
-            if (lane < half) {
-                uint16_t ka = f2bf(ra), kb = f2bf(rb);
-                if (norm) {
-                    const float *c = cs + n * rot;
-                    rope_pair(ra, rb, c[lane], c[half + lane], ka, kb);
-                }
-                if (out) {
-                    out[R + lane] = ka;
-                    out[R + lane + half] = kb;
-                }
-                if (d) {
-                    d[R + lane] = ka;
-                    d[R + lane + half] = kb;
-                }
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int c = lane + 64 * k;
+                if (c >= qr) continue;
+                if (out) *(u32x4 *)(out + 8 * c) = v[k];
+                if (d) *(u32x4 *)(d + 8 * c) = v[k];
+            }
+            // rope part: qp chunks (8 or 16 lanes), rotated without a norm
+            u32x4 r = lane < qp ? *(const u32x4 *)(yr + R + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
+            if (norm) r = rope_chunk(r, rot, csr, lane);
+            if (lane < qp) {
+                if (out) *(u32x4 *)(out + R + 8 * lane) = r;
+                if (d) *(u32x4 *)(d + R + 8 * lane) = r;
             }
         }
     }
-
 }
 
 // ---------------------------------------------------------------------------
