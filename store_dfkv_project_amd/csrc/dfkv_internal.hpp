@@ -36,10 +36,23 @@ __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
 }
 
+// v plus the value DPP control CTRL moves to this lane (rows outside ROWM add nothing).
+template <int CTRL, int ROWM = 0xF>
+__device__ __forceinline__ float dpp_add(float v) {
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWM, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wave, in every lane, by DPP moves (no LDS round trips): quad_perm
+// [1,0,3,2] and [2,3,0,1] sum each quad, row_ror:4 and :8 each row of 16, row_bcast:15 into rows
+// 1 and 3 and row_bcast:31 into rows 2 and 3 leave the total in lane 63, which is read back.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    v = dpp_add<0xB1>(v);
+    v = dpp_add<0x4E>(v);
+    v = dpp_add<0x124>(v);
+    v = dpp_add<0x128>(v);
+    v = dpp_add<0x142, 0xA>(v);
+    v = dpp_add<0x143, 0xC>(v);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 // ---------------------------------------------------------------------------
