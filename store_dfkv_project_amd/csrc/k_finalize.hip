@@ -286,8 +286,16 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
                 float ss = 0.f;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ss += v8[e] * v8[e];
+                if constexpr (HD == 128) {
+                    // a head is one DPP row of 16 lanes: quad sums, then row_ror:4 and :8
+                    ss = dpp_add<0xB1>(ss);
+                    ss = dpp_add<0x4E>(ss);
+                    ss = dpp_add<0x124>(ss);
+                    ss = dpp_add<0x128>(ss);
+                } else {
 #pragma unroll
-                for (int off = hq; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+                    for (int off = hq; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+                }
                 const float rinv = __builtin_amdgcn_rsqf(ss * inv_hd + p.nr.eps);
                 // normalised values, rounded to bf16, and the partner's
                 const u32x4 wk = *(const u32x4 *)(s_wk + l * HD + q * 8);
@@ -295,7 +303,9 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     u2[e] = pack2(bf_lo(wk[e]) * (v8[2 * e] * rinv), bf_hi(wk[e]) * (v8[2 * e + 1] * rinv));
-                    pu2[e] = (uint32_t)__shfl_xor((int)u2[e], hq, kWave);
+                    // the partner chunk is 8 lanes away inside the row of 16: row_ror:8 (HD = 128)
+                    pu2[e] = HD == 128 ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u2[e], 0x128, 0xF, 0xF, false)
+                                       : (uint32_t)__shfl_xor((int)u2[e], hq, kWave);
                 }
                 if (isk) {
                     const bool first = q < hq;
