@@ -29,12 +29,16 @@ CASES = [
     (16, MLA, 1, 4, 4, "nhd", 3, 1, 0, 2, 1024, 1024),
     (17, MLA, 4, 4, 16, "nhd", 2, 1, 0, 1, 2048, 2048),
     (18, MLA, 5, 3, 2, "nhd", 1, 1, 0, 3, 512, 1024),
+    # latent of 1024 (two 16-byte chunks per lane) and a rope part of 128 (a latent of 448)
+    (19, MLA, 2, 4, 8, "nhd", 2, 1, 0, 1, 1024, 1024, 1024, 64),
+    (20, MLA, 3, 4, 8, "nhd", 2, 1, 0, 2, 512, 1024, 448, 128),
 ]
 
 
 def _workload(case, bs=5):
-    seed, kind, B, W, pg, layout, L, nkv, hd, n_tgt, tgt_hidden, hidden = case
-    geom = small_geom(kind, L=L, nkv=nkv, hd=hd if kind == GQA else 64, R=512 if kind == MLA else 64, P=64, pg=pg,
+    seed, kind, B, W, pg, layout, L, nkv, hd, n_tgt, tgt_hidden, hidden = case[:12]
+    R, P = case[12:14] if len(case) > 12 else (512 if kind == MLA else 64, 64)
+    geom = small_geom(kind, L=L, nkv=nkv, hd=hd if kind == GQA else 64, R=R, P=P, pg=pg,
                       W=W, bs=bs, n_tgt=n_tgt, tgt_hidden=tgt_hidden, hidden=hidden)
     wl = edge_workload(seed, geom, B, transposed_tokens=bool(seed % 2), with_row_valid=seed % 3 != 0)
     rng = np.random.default_rng(seed + 500)
