@@ -271,14 +271,17 @@ dfkv_status dfkv_pack_fc_weight(const dfkv_geom *g, const void *w_fc, void *w_fc
 
 /* Write a weight w (bf16 [rows][cols] row-major, 16-byte aligned: w_fc with
  * rows = hidden, cols = n_tgt*tgt_hidden, or w_kv with rows = n_layers*per_layer,
- * cols = hidden) in the order the weight-streaming GEMMs of <= 64 rows read it:
- * element (o, k) goes to bf16 index
- *   ((k/128) * (rows/16) + o/16) * 2048 + ((k%128)/32 * 64 + (k%32)/8 * 16 + o%16) * 8 + k%8.
- * A block of 16 rows x 128 columns is 4 KB in a row, the blocks of one column
- * range sit next to each other for all row groups, and each 1 KB of a block is
- * what the 64 lanes of a wave load in one instruction: every workgroup of the
- * GEMM, which owns 16 rows, then reads whole 1 KB runs, and the workgroups
- * together sweep the weight front to back.  Done once per weight (weights are
+ * cols = hidden) in the order the weight-streaming GEMMs of <= 64 rows read it.
+ * With kb = k/128, j = kb/8, width = min(8, cols/128 - 8*j), element (o, k)
+ * goes to bf16 index
+ *   (j*8*(rows/16) + (o/16)*width + kb%8) * 2048
+ *     + ((k%128)/32 * 64 + (k%32)/8 * 16 + o%16) * 8 + k%8.
+ * A block of 16 rows x 128 columns is 4 KB in a row and each 1 KB of it is what
+ * the 64 lanes of a wave load in one instruction; the (up to) 8 blocks of one
+ * row group and 1024-column range sit next to each other (the 8 waves of a
+ * workgroup, which owns 16 rows, read them at the same time), and those runs of
+ * all row groups follow each other, so the workgroups together sweep the
+ * weight front to back.  Done once per weight (weights are
  * static); put the result in dfkv_weights.w_fc_stream or w_kv_stream.  A memory
  * layout of this library, not an operation of the method: the GEMMs'
  * arithmetic is unchanged.

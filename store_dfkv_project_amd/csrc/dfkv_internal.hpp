@@ -157,11 +157,17 @@ hipError_t launch_rope_cache(const dfkv_rope &r, float *cs, int cache_len, hipSt
 // dst = src [rows][K] (rows and K multiples of 64) in the fragment order of gemm_pack_index
 hipError_t launch_pack_rows(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t K, hipStream_t s);
 // Weight-streaming order of a [rows][cols] bf16 matrix (dfkv_pack_stream_weight): blocks of 16 rows
-// x 128 columns, column block major; inside a block, the 16-byte pieces in the order the 64 lanes of
-// a wave load them (load u of lane (q, c16) is row c16, columns (4u + q) * 8 .. + 8).
-__host__ __device__ inline int64_t stream_pack_index(int64_t o, int64_t k, int64_t rows) {
-    return ((k >> 7) * (rows >> 4) + (o >> 4)) * 2048 + ((((k & 127) >> 5) * 64 + ((k & 31) >> 3) * 16 + (o & 15)) << 3) +
-           (k & 7);
+// x 128 columns; the (up to 8) blocks of one row group and 1024-column range side by side, those
+// runs row group after row group, then the next 1024 columns; inside a block, the 16-byte pieces in
+// the order the 64 lanes of a wave load them (load u of lane (q, c16) is row c16, columns
+// (4u + q) * 8 .. + 8).  stream_block is the block of column block kb, row group ob (in 4 KB units).
+__host__ __device__ inline int64_t stream_block(int64_t kb, int64_t ob, int64_t rows, int64_t cols) {
+    const int64_t j = kb >> 3, left = (cols >> 7) - 8 * j, width = left < 8 ? left : 8;
+    return j * 8 * (rows >> 4) + ob * width + (kb & 7);
+}
+__host__ __device__ inline int64_t stream_pack_index(int64_t o, int64_t k, int64_t rows, int64_t cols) {
+    return stream_block(k >> 7, o >> 4, rows, cols) * 2048 +
+           ((((k & 127) >> 5) * 64 + ((k & 31) >> 3) * 16 + (o & 15)) << 3) + (k & 7);
 }
 hipError_t launch_pack_stream(const uint16_t *src, uint16_t *dst, int64_t rows, int64_t cols, hipStream_t s);
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);

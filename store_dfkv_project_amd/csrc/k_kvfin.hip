@@ -252,18 +252,17 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
 
     u32x4 a[D][4];
     // this lane's 16-byte piece u of k-block kb of tile t = t0 + i*groups: row t*16 + c16, columns
-    // kb*128 + (4u + q)*8 of a row-major weight; piece u*64 + q*16 + c16 of block (kb, t) of a
-    // tiled one (stream_pack_index)
-    const uint16_t *wl = p.w_tiled ? p.w + (int64_t)t0 * 2048 + (q * 16 + c16) * 8
-                                   : p.w + (int64_t)(t0 * 16 + c16) * p.K + q * 8;
-    const int64_t w_t = p.w_tiled ? (int64_t)groups * 2048 : (int64_t)groups * 16 * p.K;
-    const int64_t w_kb = p.w_tiled ? (int64_t)(p.O >> 4) * 2048 : 128;
+    // kb*128 + (4u + q)*8 of a row-major weight; piece u*64 + q*16 + c16 of block stream_block(kb, t)
+    // of a tiled one
+    const uint16_t *wl = p.w_tiled ? p.w + (q * 16 + c16) * 8 : p.w + (int64_t)(t0 * 16 + c16) * p.K + q * 8;
     const int w_u = p.w_tiled ? 512 : 32;
     auto load = [&](int slot, int f) {
         const int i = f / nbw, j = f - (f / nbw) * nbw;
         const int64_t kb = kb0 + wave + j * WAVES;
+        const uint16_t *wp = p.w_tiled ? wl + stream_block(kb, t0 + (int64_t)i * groups, p.O, p.K) * 2048
+                                       : wl + (int64_t)i * groups * 16 * p.K + kb * 128;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wl + i * w_t + kb * w_kb + u * w_u);
+        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wp + u * w_u);
     };
 #pragma unroll
     for (int d = 0; d < D; ++d)

@@ -210,9 +210,10 @@ hipError_t launch_pack_rows(const uint16_t *src, uint16_t *dst, int64_t rows, in
 __global__ __launch_bounds__(256) void k_pack_stream(const PackArgs a) {
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (t >= a.rows * (a.K >> 3)) return;
-    // t enumerates destination chunks: block (kb, ob), piece (u, q, c16)
-    const int64_t blk = t >> 8, piece = t & 255;
-    const int64_t ob = blk % (a.rows >> 4), kb = blk / (a.rows >> 4);
+    // t enumerates destination chunks: block blk = j*8*T + ob*width + w (stream_block), piece (u, q, c16)
+    const int64_t T = a.rows >> 4, blk = t >> 8, piece = t & 255;
+    const int64_t j = blk / (8 * T), rem = blk - j * 8 * T, left = (a.K >> 7) - 8 * j, width = left < 8 ? left : 8;
+    const int64_t ob = rem / width, kb = 8 * j + (rem - ob * width);
     const int u = (int)(piece >> 6), q = (int)((piece >> 4) & 3), c16 = (int)(piece & 15);
     const int64_t o = ob * 16 + c16, k = kb * 128 + (4 * u + q) * 8;
     *(u32x4 *)(a.dst + (t << 3)) = *(const u32x4 *)(a.src + o * a.K + k);

@@ -18,10 +18,11 @@
 //    dot product unchanged;
 //  * with a tiled weight (dfkv_pack_stream_weight) the same pieces come from a
 //    copy in which each 16-row x 128-column block is 4 KB in a row, ordered as
-//    the lanes load it (each load instruction reads 1 KB in a row), and the
-//    blocks of one k-block sit side by side for all tiles, so the workgroups
-//    together sweep the weight front to back (measured on MI355X: the bs=1 fc
-//    stream 20.8 -> 18.4 us for 100.8 MB);
+//    the lanes load it (each load instruction reads 1 KB in a row), the 8
+//    blocks the 8 waves read at once sit side by side (32 KB), and those runs
+//    follow each other tile by tile, so the workgroups together sweep the
+//    weight front to back (measured on MI355X: the bs=1 fc stream 20.8 -> 17.8
+//    us for 100.8 MB, the MLA fc 61.9 -> 50.9 us for 308 MB);
 //  * the waves of a workgroup take interleaved k-blocks; each wave keeps a ring
 //    of D k-blocks of weights (and activations) in flight;
 //  * fc reads its activations (hidden rows) through L2 in the register ring; its
@@ -51,10 +52,11 @@ __device__ __forceinline__ void stream_tile(const StreamParams &p, int t, int s,
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
     const int M = p.M;
     // this lane's 16-byte piece u of 128-wide k-block kb: row t*16 + c16, columns kb*128 + (4u + q)*8 of
-    // a row-major weight; piece u*64 + q*16 + c16 of block (kb, t) of a tiled one (stream_pack_index)
-    const uint16_t *wl = p.w_tiled ? p.w + (int64_t)t * 2048 + (q * 16 + c16) * 8
-                                   : p.w + (int64_t)(t * 16 + c16) * p.K + q * 8;
-    const int64_t w_kb = p.w_tiled ? (int64_t)(p.O >> 4) * 2048 : 128;
+    // a row-major weight; piece u*64 + q*16 + c16 of block stream_block(kb, t) of a tiled one
+    const uint16_t *wl = p.w_tiled ? p.w + (q * 16 + c16) * 8 : p.w + (int64_t)(t * 16 + c16) * p.K + q * 8;
+    auto wpiece = [&](int64_t kb) -> const uint16_t * {
+        return p.w_tiled ? wl + stream_block(kb, t, p.O, p.K) * 2048 : wl + kb * 128;
+    };
     const int w_u = p.w_tiled ? 512 : 32;
     const int kb0 = s * p.nbs;  // first k-block (128 wide) of the split
     const int kc = p.nbs * 128, ldg = kc + 8;
@@ -64,8 +66,9 @@ __device__ __forceinline__ void stream_tile(const StreamParams &p, int t, int s,
     u32x4 b[STAGE ? 1 : D][NG][4];
     auto load = [&](int slot, int j) {
         const int64_t kb = kb0 + wave + j * WAVES, k = kb * 128;
+        const uint16_t *wp = wpiece(kb);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wl + kb * w_kb + u * w_u);
+        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wp + u * w_u);
         if (!STAGE) {
 #pragma unroll
             for (int ng = 0; ng < NG; ++ng) {

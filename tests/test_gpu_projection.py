@@ -235,10 +235,11 @@ def test_pack_fc_weight_layout(H, K):
     assert torch.equal(pk, want)
 
 
-@pytest.mark.parametrize("rows,cols", [(16, 128), (48, 384), (1728, 7168), (4096, 12288)])
+@pytest.mark.parametrize("rows,cols", [(16, 128), (48, 384), (32, 1280), (1728, 7168), (4096, 12288)])
 def test_pack_stream_weight_layout(rows, cols):
-    """dfkv_pack_stream_weight puts element (o, k) where the header's formula says: checked against the same
-    permutation written as a reshape of the [rows][cols] matrix."""
+    """dfkv_pack_stream_weight puts element (o, k) where the header's formula says: the formula evaluated
+    for every element on the host, and, for whole 1024-column ranges, the same permutation written as a
+    reshape of the [rows][cols] matrix."""
     import torch
     from store_dfkv_project_amd import dfkv
     gen = torch.Generator(device="cuda")
@@ -247,9 +248,18 @@ def test_pack_stream_weight_layout(rows, cols):
     st = torch.empty_like(w)
     dfkv.dfkv_pack_stream_weight(rows, cols, w, st)
     torch.cuda.synchronize()
-    # o = 16 ob + c16, k = 128 kb + 32 u + 8 q + e  ->  [kb][ob][u][q][c16][e]
-    want = w.view(rows // 16, 16, cols // 128, 4, 4, 8).permute(2, 0, 3, 4, 1, 5).reshape(rows, cols)
-    assert torch.equal(st, want)
+    o = torch.arange(rows, device="cuda", dtype=torch.int64)[:, None]
+    k = torch.arange(cols, device="cuda", dtype=torch.int64)[None, :]
+    kb, j = k // 128, k // 1024
+    width = torch.clamp(cols // 128 - 8 * j, max=8)
+    block = j * 8 * (rows // 16) + (o // 16) * width + kb % 8
+    idx = block * 2048 + ((k % 128) // 32 * 64 + (k % 32) // 8 * 16 + o % 16) * 8 + k % 8
+    flat = st.reshape(-1)
+    assert torch.equal(flat[idx.reshape(-1)], w.reshape(-1))
+    if cols % 1024 == 0:
+        # o = 16 ob + c16, k = 1024 j + 128 w + 32 u + 8 q + e  ->  [j][ob][w][u][q][c16][e]
+        want = w.view(rows // 16, 16, cols // 1024, 8, 4, 4, 8).permute(2, 0, 3, 4, 5, 1, 6).reshape(rows, cols)
+        assert torch.equal(st, want)
 
 
 # row counts through every weight-streaming kernel: the staged K/V groups (<= 16 rows) and the
