@@ -18,9 +18,11 @@ runs ahead of the GPU.
 Dominant kernel: the fc GEMM (k_stream at <= 64 rows, k_gemm above), timed
 as back-to-back dfkv_project_fc launches inside one graph; the K/V stage
 (dfkv_project_kv) is timed the same way and reported beside it.  At <= 16 rows
-the step is two kernels (fc, then K/V with the finalize, store and advance in
-one launch); the staged path (dfkv_project_fc + dfkv_project_kv +
-dfkv_store_advance) is timed as well for comparison.
+the step is three kernels (fc; the K/V GEMM groups; the finalize with the
+store and advance); the staged path (dfkv_project_fc + dfkv_project_kv +
+dfkv_store_advance) is timed as well for comparison.  At <= 64 rows every
+weight copy comes with its tiled copies (dfkv_pack_stream_weight), which the
+streaming GEMMs read.
 
 Prints ONE JSON line.  --gpus N > 1 is refused: this path runs on one GPU.
 """
@@ -434,7 +436,7 @@ def main() -> int:
         traffic = measured_traffic() if args.config == 1 and wl.n_rows == 4 else None
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
-                    kernel="k_stream<fc> (dfkv_project_fc: the fc GEMM streaming w_fc, f + row statistics)",
+                    kernel="k_stream<fc> (dfkv_project_fc: the fc GEMM streaming the tiled w_fc, f + row statistics)",
                     algorithmic_bytes_per_launch=alg["fc_bytes"])
     else:
         achieved = alg["fc_flops"] / (fc_mean * 1e-6) / 1e12
