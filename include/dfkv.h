@@ -306,7 +306,9 @@ dfkv_status dfkv_pack_stream_weight(int64_t rows, int64_t cols, const void *w, v
  *          elements used; rows 16-byte aligned.
  *  kv_out: bf16 [N][O] contiguous, 16-byte aligned; must not overlap hidden,
  *          the weights, cos_sin or ws.
- *  cos_sin/cache_len: needed only with DFKV_FUSE_NORM_ROPE.
+ *  ctx_len_in, cos_sin/cache_len, w->w_knorm: needed only with
+ *          DFKV_FUSE_NORM_ROPE; without it they may be NULL / 0 and are not
+ *          read.
  *  ws: >= dfkv_workspace_size bytes of device memory.
  * Errors: NULL, SHAPE, LAYOUT, ALIAS, WORKSPACE, HIP. */
 dfkv_status dfkv_project(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,

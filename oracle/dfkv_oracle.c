@@ -221,6 +221,9 @@ EXPORT void dfkv_oracle_rope_cache(double theta, int rot, int yarn, double facto
     for (int p = 0; p < cache_len; ++p) {
         for (int i = 0; i < half; ++i) {
             double a = (double)p * inv[i];
+#if DFKV_ORACLE_MUTANT == 12 /* planted: the angle formed in fp32 */
+            a = (double)((float)p * (float)inv[i]);
+#endif
             cs[(int64_t)p * rot + i] = (float)(cos(a) * m);
             cs[(int64_t)p * rot + half + i] = (float)(sin(a) * m);
         }

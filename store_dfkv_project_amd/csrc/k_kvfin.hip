@@ -243,7 +243,9 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     const FinalizeParams &fin = kp.fin;
     const int groups = kp.n_groups / p.S;
     const int s = blockIdx.x / groups, t0 = blockIdx.x - s * groups;   // tiles t0 + i*groups
-    const bool book = blockIdx.x == 0;
+    // group 0 gathers the rows' and requests' fields, but only for a call that uses them: an
+    // unfused projection (no norm, store or advance) may pass no ctx_len_in at all
+    const bool book = blockIdx.x == 0 && (fin.norm || fin.store || fin.advance);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
     const int M = p.M, ntg = kp.ntg;
     const int kb0 = s * p.nbs, kc = p.nbs * 128, ldg = kc + 8;

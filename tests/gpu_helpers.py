@@ -25,7 +25,11 @@ def assert_close_bf16(got_bits, ref_bits, what: str = "", atol: float = ATOL, rt
     bound = atol + rtol * np.abs(r)
     bad = err > bound
     rel = err / np.maximum(np.abs(r), 1e-6)
+    # the bound read literally, each part alone: elements off by more than 2e-2, and the largest
+    # relative error where the relative part is the tighter one (|ref| >= 2)
+    big = np.abs(r) >= 2.0
     stats = dict(max_abs=float(err.max(initial=0.0)), max_rel_of_large=float(rel[np.abs(r) > 0.1].max(initial=0.0)),
+                 max_rel_ref_ge_2=float(rel[big].max(initial=0.0)), n_abs_over_2e_2=int((err > atol).sum()),
                  n=int(err.size))
     if bad.any():
         i = np.argmax(err - bound)

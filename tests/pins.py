@@ -185,6 +185,28 @@ def pin_rope_cache_special_rows(o):
         assert cs[p, 0] == np.float32(math.cos(p)) and cs[p, 32] == np.float32(math.sin(p))
 
 
+def pin_rope_cache_long_positions(o):
+    """Far into the context (positions 131071, 262144, 393216) every entry of the cache is
+    m*cos(p*inv_i) / m*sin(p*inv_i) from an fp64 angle, rounded once to fp32: checked against Python's
+    math.cos/math.sin of p*inv_i in fp64 (inv_i and m from inv_freq, which the YaRN pins fix), for plain
+    RoPE and both YaRN specs of the workloads.  An angle formed in fp32 is off by up to half an fp32
+    spacing of p*inv_i (about 4e-6 rad at 131 rad), hundreds of fp32 spacings of the value."""
+    positions = (131071, 262144, 393216)
+    for rope in (RopeSpec(theta=1e6, rot=128),
+                 RopeSpec(theta=1e6, rot=64, yarn=True, factor=40.0, orig_ctx=4096.0),
+                 RopeSpec(theta=1e6, rot=128, yarn=True, factor=4.0, orig_ctx=32768.0)):
+        half = rope.rot // 2
+        cs = o.rope_cache(rope, positions[-1] + 1)
+        inv, m = o.inv_freq(rope)
+        for p in positions:
+            want = np.array([m * math.cos(p * f) for f in inv] + [m * math.sin(p * f) for f in inv],
+                            dtype=np.float64)
+            got = cs[p].astype(np.float64)
+            tol = np.spacing(np.abs(want).astype(np.float32)).astype(np.float64)
+            bad = np.nonzero(np.abs(got - want) > tol)[0]
+            assert bad.size == 0, (rope, p, int(bad[0]) % half, got[bad[0]], want[bad[0]])
+
+
 def pin_rope_complex_rotation(o):
     """A NeoX pair (u_j, u_{j+h}) is the complex number u_j + i*u_{j+h}; RoPE multiplies it by exp(i*p*inv_j)."""
     rng = np.random.default_rng(31)

@@ -1,8 +1,9 @@
 """The five workloads at full size through dfkv_step (the launch configuration
 the benchmark times): bookkeeping of every row bit-exact, the pool byte-exact
 (destinations hold the step's K/V rows, everything else keeps its random
-pre-image), and projected K/V of sampled rows -- spread over tiles, including
-the last rows -- within |d| <= 2e-2 + 1e-2*|ref| of the oracle.  Also: replay of
+pre-image), and projected K/V of every row within |d| <= 2e-2 + 1e-2*|ref| of
+the oracle (every token tile and k-split of the large-batch GEMMs, up to the
+4096 rows of the stress workload).  Also: replay of
 a captured graph against the eager step, and the NaN padding of strided
 hidden rows never reaching the output."""
 import numpy as np
@@ -16,14 +17,7 @@ pytestmark = pytest.mark.gpu
 RUNS = [(0, None), (1, 2048), (1, 32768), (2, None), (3, 2048), (3, 131072), (3, 393216), (4, None)]
 
 
-def _sample_rows(N: int, k: int = 24) -> np.ndarray:
-    if N <= k:
-        return np.arange(N, dtype=np.int32)
-    rng = np.random.default_rng(N)
-    pick = set(rng.choice(N, size=k - 4, replace=False).tolist()) | {0, 1, N - 2, N - 1}
-    return np.array(sorted(pick), dtype=np.int32)
-
-
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("cfg,ctx", RUNS, ids=[f"c{c}" + (f"-ctx{x}" if x else "") for c, x in RUNS])
 def test_step_full_size(orc, cfg, ctx):
     import torch
@@ -39,11 +33,11 @@ def test_step_full_size(orc, cfg, ctx):
     exp = expected_pool_torch(ds, before, ds.kv_out, want["slot"], want["write_mask"])
     assert torch.equal(ds.pool_t, exp), "pool differs: a destination is missing or a non-destination changed"
     del exp, before
-    rows = _sample_rows(wl.n_rows)
     cs = orc.rope_cache(wl.rope, wl.cache_len)
-    ref = orc.project(wl.geom, wl.hidden, wl.w_fc, wl.w_hnorm, wl.w_kv, wl.w_knorm, wl.ctx_len, cs, row_ids=rows)
-    got = ds.bits(ds.kv_out)[rows]
-    stats = assert_close_bf16(got, ref["kv"], f"config {cfg} kv rows {rows.tolist()[:6]}...")
+    print(f"[step] config {cfg}: oracle projection of all {wl.n_rows} rows", flush=True)
+    ref = orc.project(wl.geom, wl.hidden, wl.w_fc, wl.w_hnorm, wl.w_kv, wl.w_knorm, wl.ctx_len, cs)
+    got = ds.bits(ds.kv_out)
+    stats = assert_close_bf16(got, ref["kv"], f"config {cfg} kv (all {wl.n_rows} rows)")
     print(f"[step] config {cfg} ctx={ctx}: {stats}", flush=True)
     if cfg == 4:   # strided hidden rows carry NaN padding: the output must stay finite
         assert np.isfinite(

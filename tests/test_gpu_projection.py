@@ -332,3 +332,30 @@ def test_packed_fc_weight_same_bits(orc, name, geom, B):
     ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
     torch.cuda.synchronize()
     assert torch.equal(packed, ds.kv_out), "packed and row-major fc weights give different bits"
+
+
+@pytest.mark.parametrize("geom,B", [(GQA_G, 1), (GQA_G, 4), (MLA_G, 3)], ids=["gqa128-B1", "gqa128-B4", "mla-B3"])
+def test_unfused_project_without_ctx(orc, geom, B):
+    """An unfused projection (flags 0) needs no context lengths, cos/sin cache or k_norm weights, and
+    the header lets a caller pass NULL for them: the call is accepted, the small-batch K/V kernels
+    (<= 16 rows) read none of them, and y matches the oracle -- through dfkv_project and through the
+    two stages."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    rope = RopeSpec(theta=1e6, rot=geom.rope_dim)
+    wl, ds, ref = _run_case(orc, "no-ctx", geom, B, rope)
+    assert ds.N <= 16
+    w_fc, w_hn, w_kv, _ = ds.weights[0]
+    fs, ks = ds.w_stream[0]
+    no_kn = dfkv.make_weights(w_fc, w_hn, w_kv, None, w_fc_stream=fs, w_kv_stream=ks)
+    ds.kv_out.fill_(0x7FC0)
+    dfkv.dfkv_project(ds.gs, no_kn, ds.hidden, wl.hidden_row_stride, wl.n_reqs, None, None, 0, ds.kv_out, 0,
+                      ds.ws, ds.ws_bytes)
+    torch.cuda.synchronize()
+    assert_close_bf16(ds.bits(ds.kv_out), ref["y"], "dfkv_project without ctx_len_in")
+    first = ds.kv_out.clone()
+    ds.kv_out.fill_(0x7FC0)
+    dfkv.dfkv_project_fc(ds.gs, no_kn, ds.hidden, wl.hidden_row_stride, wl.n_reqs, ds.ws, ds.ws_bytes)
+    dfkv.dfkv_project_kv(ds.gs, no_kn, wl.n_reqs, None, None, 0, ds.kv_out, 0, ds.ws, ds.ws_bytes)
+    torch.cuda.synchronize()
+    assert torch.equal(first, ds.kv_out), "staged unfused projection differs"
