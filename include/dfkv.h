@@ -231,7 +231,8 @@ const char *dfkv_version(void);
 const char *dfkv_hip_error_string(void);
 
 /* Bytes of workspace dfkv_project / dfkv_step need for n_reqs requests
- * (split-K partials, row statistics, tile tickets).  Writes *bytes.
+ * (f and its row statistics, split-K partials, the K/V stage's bookkeeping
+ * hand-off).  Writes *bytes.
  * Errors: NULL if g or bytes is NULL; SHAPE for an unsupported geometry. */
 dfkv_status dfkv_workspace_size(const dfkv_geom *g, int32_t n_reqs, size_t *bytes);
 
@@ -469,6 +470,25 @@ dfkv_status dfkv_step(const dfkv_geom *g, const dfkv_weights *w, const void *hid
                       int64_t hidden_row_stride, const dfkv_requests *req, const float *cos_sin,
                       int32_t cache_len, void *kv_out, const dfkv_pool *pool, const dfkv_outputs *out,
                       void *ws, size_t ws_bytes, dfkv_stream_t stream);
+
+/* dfkv_step for callers that cannot allocate (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same arguments, kernels
+ * and results, without ws/ws_bytes -- the workspace is a static device array of
+ * DFKV_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call there).  Allocates nothing.  The array carries nothing that a
+ * call reads from one call to the next.  Every call on one GPU shares that
+ * GPU's array: two calls that overlap on one GPU (on different streams, or
+ * concurrently from several host threads) race and must not be issued.
+ * Errors as dfkv_step; WORKSPACE when the call's workspace
+ * (dfkv_workspace_size) exceeds DFKV_NOALLOC_SCRATCH_BYTES -- every plan of up
+ * to 64 rows of the workloads' drafters fits; HIP when the array's address
+ * cannot be obtained. */
+enum { DFKV_NOALLOC_SCRATCH_BYTES = 8 << 20 };
+dfkv_status dfkv_step_noalloc(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
+                              int64_t hidden_row_stride, const dfkv_requests *req, const float *cos_sin,
+                              int32_t cache_len, void *kv_out, const dfkv_pool *pool, const dfkv_outputs *out,
+                              dfkv_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -3,9 +3,17 @@
 // a refused call launches nothing and writes nothing.
 #include <string.h>
 
+#include <mutex>
+
 #include "dfkv_internal.hpp"
 
 using namespace dfkv;
+
+// Device scratch of dfkv_step_noalloc: the workspace of a call that cannot allocate.  Each GPU the
+// library runs on holds its own copy until the process ends.  Host code never uses this name as an
+// address (on the host it is only a stand-in for the symbol); it uses the per-device address that
+// scratch_address() looks up.
+static __device__ __align__(256) uint8_t scratch[DFKV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -140,6 +148,40 @@ struct Plan {
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Per-device address of `scratch`, looked up once per device (hipGetSymbolAddress with that device
+// current) and kept.  The device is the stream's (the current device for the null stream).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_addr[kMaxDevices];
+
+hipError_t scratch_address(hipStream_t s, void **out) {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (s) {
+        hipDevice_t sd = 0;
+        if ((e = hipStreamGetDevice(s, &sd)) != hipSuccess) return e;
+        dev = (int)sd;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        g_scratch_addr[dev] = ptr;
+    }
+    *out = g_scratch_addr[dev];
+    return hipSuccess;
+}
 
 dfkv_status make_plan(const dfkv_geom *g, int32_t n_reqs, Plan *pl) {
     dfkv_status st = check_geom(g);
@@ -929,6 +971,24 @@ dfkv_status dfkv_step(const dfkv_geom *g, const dfkv_weights *w, const void *hid
     fin.advance = 1;
     return run_project(g, w, hidden, hidden_row_stride, req->ctx_len_in, cos_sin, cache_len, kv_out, true, ws, pl,
                        fin, true, (hipStream_t)stream);
+}
+
+dfkv_status dfkv_step_noalloc(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,
+                              int64_t hidden_row_stride, const dfkv_requests *req, const float *cos_sin,
+                              int32_t cache_len, void *kv_out, const dfkv_pool *pool, const dfkv_outputs *out,
+                              dfkv_stream_t stream) {
+    if (!g || !req) return DFKV_ERR_NULL;
+    Plan pl;
+    dfkv_status st = make_plan(g, req->n_reqs, &pl);
+    if (st != DFKV_OK) return st;
+    if (pl.total > (size_t)DFKV_NOALLOC_SCRATCH_BYTES) return DFKV_ERR_WORKSPACE;
+    void *ws = nullptr;
+    const hipError_t e = scratch_address((hipStream_t)stream, &ws);
+    if (e != hipSuccess) return hip_status(e);
+    // the same validation and kernels as dfkv_step, on this device's scratch (nothing in it needs
+    // clearing: every byte a kernel reads there was written earlier in the same call)
+    return dfkv_step(g, w, hidden, hidden_row_stride, req, cos_sin, cache_len, kv_out, pool, out, ws,
+                     (size_t)DFKV_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -26,6 +26,7 @@ DFKV_ERR_LAYOUT = -3
 DFKV_ERR_ALIAS = -4
 DFKV_ERR_WORKSPACE = -5
 DFKV_ERR_HIP = -6
+DFKV_NOALLOC_SCRATCH_BYTES = 8 << 20   # include/dfkv.h: the static scratch of dfkv_step_noalloc
 
 DFKV_GQA = 0
 DFKV_MLA = 1
@@ -35,7 +36,8 @@ DFKV_FUSE_NORM_ROPE = 1
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",
             "dfkv_store_advance", "dfkv_step", "dfkv_project_fork", "dfkv_join", "dfkv_block_table_decode",
-            "dfkv_strict_accept", "dfkv_paged_store_rows", "dfkv_pack_fc_weight", "dfkv_pack_stream_weight")
+            "dfkv_strict_accept", "dfkv_paged_store_rows", "dfkv_pack_fc_weight", "dfkv_pack_stream_weight",
+            "dfkv_step_noalloc")
 
 
 class dfkv_geom(C.Structure):
@@ -117,6 +119,7 @@ def _load() -> C.CDLL:
         "dfkv_advance": ([gp, rp, op, P], C.c_int),
         "dfkv_store_advance": ([gp, P, rp, pp, op, P], C.c_int),
         "dfkv_step": ([gp, wp, P, I64, rp, P, I32, P, pp, op, P, SZ, P], C.c_int),
+        "dfkv_step_noalloc": ([gp, wp, P, I64, rp, P, I32, P, pp, op, P], C.c_int),
         "dfkv_project_fork": ([gp, wp, P, I64, I32, P, P, I32, P, U32, P, SZ, P, P, P, P], C.c_int),
         "dfkv_join": ([P, P], C.c_int),
         "dfkv_block_table_decode": ([P, I64, I64, I32, I32, P, I32, I32, P, P, I64, P], C.c_int),
@@ -337,3 +340,10 @@ def dfkv_step(geom, weights, hidden, hidden_row_stride, requests, cos_sin, cache
     _check(_lib.dfkv_step(_ref(geom), _ref(weights), _ptr(hidden), int(hidden_row_stride), _ref(requests),
                           _ptr(cos_sin), int(cache_len), _ptr(kv_out), _ref(pool), _ref(outputs), _ptr(ws),
                           int(ws_bytes), _stream(stream)), "dfkv_step")
+
+
+def dfkv_step_noalloc(geom, weights, hidden, hidden_row_stride, requests, cos_sin, cache_len, kv_out, pool, outputs,
+                      stream=None) -> None:
+    _check(_lib.dfkv_step_noalloc(_ref(geom), _ref(weights), _ptr(hidden), int(hidden_row_stride), _ref(requests),
+                                  _ptr(cos_sin), int(cache_len), _ptr(kv_out), _ref(pool), _ref(outputs),
+                                  _stream(stream)), "dfkv_step_noalloc")

@@ -382,3 +382,19 @@ def test_norm_rope_validation():
         dfkv.DFKV_ERR_ALIAS
     assert status_of(dfkv.dfkv_norm_rope, g, addr(4), 1, addr(6), addr(7), 0, addr(8), stream=0) == \
         dfkv.DFKV_ERR_SHAPE
+
+
+def test_step_noalloc_validation():
+    """The static-scratch step refuses, before touching a GPU, a plan larger than its scratch (the dense
+    drafter at 64 requests of 16 rows needs about 84 MB) and NULL geometry or requests."""
+    g = geom(width=16)
+    assert dfkv.dfkv_workspace_size(g, 64) > dfkv.DFKV_NOALLOC_SCRATCH_BYTES
+    assert dfkv.dfkv_workspace_size(geom(), 16) <= dfkv.DFKV_NOALLOC_SCRATCH_BYTES
+    assert dfkv.dfkv_workspace_size(mla_geom(), 16) <= dfkv.DFKV_NOALLOC_SCRATCH_BYTES
+    w = dfkv.make_weights(addr(1), addr(2), addr(3), addr(4))
+    base = dict(geom=g, weights=w, hidden=addr(5), hidden_row_stride=12288, requests=requests(n_reqs=64),
+                cos_sin=addr(7), cache_len=4096, kv_out=addr(8), pool=pool(), outputs=outputs(), stream=0)
+    assert status_of(dfkv.dfkv_step_noalloc, **base) == dfkv.DFKV_ERR_WORKSPACE
+    assert status_of(dfkv.dfkv_step_noalloc, **dict(base, geom=None)) == dfkv.DFKV_ERR_NULL
+    assert status_of(dfkv.dfkv_step_noalloc, **dict(base, requests=None)) == dfkv.DFKV_ERR_NULL
+    assert status_of(dfkv.dfkv_step_noalloc, **dict(base, geom=geom(kind=2))) == dfkv.DFKV_ERR_SHAPE
