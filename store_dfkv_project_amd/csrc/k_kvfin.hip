@@ -66,26 +66,29 @@ __device__ __forceinline__ float *book_cs(void *b) { return (float *)((char *)b 
 // instead of after it.
 __device__ __forceinline__ void kvfinal_bookkeeping(const FinalizeParams &p, void *book) {
     const int tid = threadIdx.x, Mall = p.M;
-    if (p.store && tid < Mall) {
-        const int64_t slot = book_slot(book)[tid];
+    // every load first (one round), then the stores: rows (slot, context position; tid < M <= 16),
+    // block positions (embedding id, query position; tid < B*block_size <= 384), requests (tid < B)
+    const int32_t *ctx = book_ctx(book), *ctx_new = book_ctx_new(book), *bonus = book_bonus(book);
+    const bool row = tid < Mall, blk = p.advance && tid < p.B * p.bs_blk, req = p.advance && tid < p.B;
+    const int rr = row ? tid / p.W : 0, ri = row ? tid - rr * p.W : 0;
+    const int br = blk ? tid / p.bs_blk : 0, bj = blk ? tid - br * p.bs_blk : 0;
+    const int64_t slot = row && p.store ? book_slot(book)[tid] : -1;
+    const int32_t c = row && p.advance ? ctx[rr] : 0;
+    const int32_t b_bonus = blk ? bonus[br] : 0, b_cn = blk ? ctx_new[br] : 0;
+    const int32_t r_bonus = req ? bonus[tid] : 0, r_cn = req ? ctx_new[tid] : 0;
+    if (row && p.store) {
         p.slot[tid] = slot;
         p.wmask[tid] = slot >= 0 ? 1 : 0;
     }
-    if (!p.advance) return;
-    const int32_t *ctx = book_ctx(book), *ctx_new = book_ctx_new(book), *bonus = book_bonus(book);
-    for (int e = tid; e < Mall; e += kKvThreads) {
-        const int r = e / p.W, i = e - (e / p.W) * p.W;
-        p.c_pos[e] = (int32_t)((int64_t)ctx[r] + i);
+    if (row && p.advance) p.c_pos[tid] = (int32_t)((int64_t)c + ri);
+    if (blk) {
+        p.emb[tid] = bj == 0 ? b_bonus : p.mask_id;
+        p.q_pos[tid] = b_cn + bj;
     }
-    for (int e = tid; e < p.B * p.bs_blk; e += kKvThreads) {
-        const int r = e / p.bs_blk, j = e - (e / p.bs_blk) * p.bs_blk;
-        p.emb[e] = j == 0 ? bonus[r] : p.mask_id;
-        p.q_pos[e] = ctx_new[r] + j;
-    }
-    if (tid < p.B) {
-        p.bonus[tid] = bonus[tid];
-        p.ctx_out[tid] = ctx_new[tid];
-        p.seq_len[tid] = ctx_new[tid] + p.bs_blk;
+    if (req) {
+        p.bonus[tid] = r_bonus;
+        p.ctx_out[tid] = r_cn;
+        p.seq_len[tid] = r_cn + p.bs_blk;
     }
 }
 
@@ -124,10 +127,29 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     float *cs = (float *)((char *)sh_dyn + kp.lds_cs);           // [M][rot]
     __shared__ int64_t sh_slot[kKvMaxRows];
 
-    // phase A
+    // phase A, one round of loads: the unit's k_norm weights, the rows' cos/sin values and slots are
+    // issued first (into registers), then the split partials; everything lands in LDS after the
+    // partials' wait (loads issued as separate loops would each wait for their own hop)
     constexpr int EB = 2;   // elements per thread per round
     constexpr int SB = 8;   // splits per round
+    constexpr int WKN = 1024 / kKvThreads;               // k_norm weights per thread (nwk <= 1024)
+    constexpr int CSF = kKvWaves * 256 / kKvThreads;     // cos/sin values per thread (<= 8 rows x 256)
     const int total = M * cols;
+    uint16_t wkv[WKN];
+    float csv[CSF];
+    const uint16_t *wsrc = p.nr.w_knorm + (int64_t)l * nwk;
+    const float *bcs = book_cs(book) + (int64_t)n0 * rot;
+#pragma unroll
+    for (int k = 0; k < WKN; ++k) {
+        const int c = tid + k * kKvThreads;
+        wkv[k] = norm && c < nwk ? wsrc[c] : (uint16_t)0;
+    }
+#pragma unroll
+    for (int k = 0; k < CSF; ++k) {
+        const int e = tid + k * kKvThreads;
+        csv[k] = norm && e < M * rot ? bcs[e] : 0.f;
+    }
+    const int64_t slotv = tid < M && p.store ? book_slot(book)[n0 + tid] : -1;
     for (int e0 = tid; e0 < total; e0 += EB * kKvThreads) {
         float acc[EB] = {0.f, 0.f};
         for (int s0 = 0; s0 < S; s0 += SB) {
@@ -154,12 +176,18 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
         }
     }
     if (norm) {
-        const uint16_t *w = p.nr.w_knorm + (int64_t)l * nwk;
-        for (int c = tid; c < nwk; c += kKvThreads) wk[c] = w[c];
-        const float *bcs = book_cs(book) + (int64_t)n0 * rot;
-        for (int e = tid; e < M * rot; e += kKvThreads) cs[e] = bcs[e];
+#pragma unroll
+        for (int k = 0; k < WKN; ++k) {
+            const int c = tid + k * kKvThreads;
+            if (c < nwk) wk[c] = wkv[k];
+        }
+#pragma unroll
+        for (int k = 0; k < CSF; ++k) {
+            const int e = tid + k * kKvThreads;
+            if (e < M * rot) cs[e] = csv[k];
+        }
     }
-    if (tid < M) sh_slot[tid] = p.store ? book_slot(book)[n0 + tid] : -1;
+    if (tid < M) sh_slot[tid] = slotv;
     __syncthreads();
 
     // phase B: one wave per row, 16-byte chunks (lane L holds elements 8L .. 8L+7 of a head, of the
