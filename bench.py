@@ -51,7 +51,9 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stream_fc_dense_bs1_hbm_counters.md")
+# copy-calibrated FETCH_SIZE + WRITE_SIZE of the dominant (fc) stage, per workload the counters were taken on
+TRAFFIC_FILES = {1: os.path.join(ROOT, "profiles", "k_stream_fc_dense_bs1_hbm_counters.md"),
+                 2: os.path.join(ROOT, "profiles", "k_gemm_dense_bs64_hbm_counters.md")}
 
 
 def source_digest() -> str:
@@ -69,11 +71,14 @@ def source_digest() -> str:
     return h.hexdigest()
 
 
-def measured_traffic():
-    """HBM bytes per fc launch from the committed FETCH_SIZE/WRITE_SIZE summary (copy-calibrated), or None
-    when it is absent or was taken on kernel sources other than the current ones."""
+def measured_traffic(cfg: int):
+    """HBM bytes per fc-stage launch from the committed FETCH_SIZE/WRITE_SIZE summary of workload `cfg`
+    (copy-calibrated), or None when there is none or it was taken on kernel sources other than the
+    current ones."""
+    if cfg not in TRAFFIC_FILES:
+        return None
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILES[cfg]).read()
     except OSError:
         return None
     vals = {}
@@ -482,7 +487,7 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
     if wl.n_rows <= 64:
         achieved = alg["fc_bytes"] / (fc_mean * 1e-6) / 1e9
         # the counters were taken on the bs=1 dense workload at 32768 context; other workloads report null
-        traffic = measured_traffic() if cfg == 1 and wl.n_rows == 4 else None
+        traffic = measured_traffic(cfg) if cfg == 1 and ctx == 32768 else None
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="k_stream<fc> (dfkv_project_fc: the fc GEMM streaming the tiled w_fc, f + row statistics)",
@@ -490,7 +495,7 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
     else:
         achieved = alg["fc_flops"] / (fc_mean * 1e-6) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
+                    frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=measured_traffic(cfg),
                     kernel="fc stage (dfkv_project_fc: k_gemm on the packed w_fc, then hidden_norm)",
                     algorithmic_flops_per_launch=alg["fc_flops"])
     roof.update(launch_us_mean=round(fc_mean, 2), launch_us_p10=round(float(np.percentile(fc_us, 10)), 2),
