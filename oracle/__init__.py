@@ -22,12 +22,15 @@ SRC = os.path.join(HERE, "dfkv_oracle.c")
 LIB = os.path.join(HERE, "libdfkv_oracle.so")
 
 
-def build(out: str = LIB, mutant: int = 0, openmp: bool = True) -> str:
-    """Compile the oracle with gcc (plain -O2: no fast-math, no reassociation)."""
+def build(out: str = LIB, mutant: int = 0, openmp: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc (plain -O2: no fast-math, no reassociation).  sanitize: with
+    AddressSanitizer and UndefinedBehaviorSanitizer (the loading process must preload libasan)."""
     cmd = ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-fPIC", "-shared", "-fvisibility=hidden",
            f"-DDFKV_ORACLE_MUTANT={int(mutant)}", SRC, "-o", out + ".tmp", "-lm"]
     if openmp:
         cmd.insert(1, "-fopenmp")
+    if sanitize:
+        cmd[1:1] = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
     subprocess.run(cmd, check=True)
     os.replace(out + ".tmp", out)
     return out

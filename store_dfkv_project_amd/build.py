@@ -20,9 +20,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: libdfkv needs the ROCm toolchain")
 
 
-def command(out: str = LIB, defines=()) -> list:
+def command(out: str = LIB, defines=(), sanitize: bool = False) -> list:
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+    # sanitize: the host code (validation, planning, dispatch) with AddressSanitizer and
+    # UndefinedBehaviorSanitizer; the GPU code is built as always
+    san = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all"] if sanitize else []
+    return [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared", *san,
             *[f"-D{d}" for d in defines],
             # packed fp32 instructions are kept out of every kernel (hipcc's host pass
             # warns that it does not know the feature; that is expected)
@@ -30,9 +34,9 @@ def command(out: str = LIB, defines=()) -> list:
             "-Wno-unused-result", *srcs, "-o", out]
 
 
-def build(out: str = LIB, verbose: bool = False, defines=()) -> str:
+def build(out: str = LIB, verbose: bool = False, defines=(), sanitize: bool = False) -> str:
     tmp = out + ".tmp"
-    cmd = command(tmp, defines)
+    cmd = command(tmp, defines, sanitize)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
