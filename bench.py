@@ -15,8 +15,10 @@ consecutive steps (d = the smallest divisor of --steps that is at least 8, else
 --steps), rotating over 4 copies of the weights (each copy is reused only
 after the 3 others, and 4 x the weight bytes exceed the 256 MiB Infinity Cache,
 so every step streams its weights from HBM; the graphs continue the rotation
-across replay boundaries).  HIP events bracket every replay on its stream; a
-spin kernel is queued first so the host runs ahead of the GPU.  A step sits
+across replay boundaries).  HIP events bracket every replay on its stream; the
+warm-up replays (at least --warmup steps and about 20 ms of work, so the clocks
+have settled) are queued right before the timed ones with no synchronisation
+between, so the GPU never waits for the host.  A step sits
 inside the serving loop's own graph, so a per-step graph launch is excluded
 from the headline and reported apart (us_per_step_single_graph_replay); 24
 further replays give the spread (p10 / median / p90).
@@ -439,9 +441,9 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
 
     # one graph of d steps per starting weight copy, so that replay j (starting at copy j*d mod R)
     # continues the rotation of replay j-1: no copy is used twice in a row across a replay boundary
-    starts = sorted({(j * d) % R for j in range(max(n_rep, R))})
+    starts = sorted({(j * d) % R for j in range(R)})
     g_steps = {s0: capture(lambda c: ds.step(copy=c), d, s0) for s0 in starts}
-    order = [g_steps[(j * d) % R] for j in range(n_rep)]
+    order = lambda j: g_steps[(j * d) % R]   # replay j starts at copy j*d mod R
     g_single = [capture(lambda c: ds.step(copy=c), 1, c) for c in range(R)]
     g_fc = capture(lambda c: ds.project_fc(copy=c), FC_PER_GRAPH)
     g_kv = capture(lambda c: ds.project_kv(copy=c), FC_PER_GRAPH)
@@ -449,24 +451,33 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
     torch.cuda.synchronize()
     accepted = int(ds.write_mask.sum().item())
 
-    def timed(graphs, replays, warm, per_replay):
-        """HIP events around every replay on the replay stream; returns per-unit us (replay / per_replay)."""
+    def timed(graphs, replays, warm, per_replay, min_warm_ms=20.0):
+        """HIP events around every replay on the replay stream; returns per-unit us (replay / per_replay).
+        `graphs`: a list, cycled, or a function of the replay's index.  The warm-up replays (at least
+        `warm`, and about min_warm_ms of GPU work, so that the clocks have settled) run back to back
+        right before the timed ones, with no synchronisation between: the GPU stays busy while the host
+        queues the timed replays, and the replay index carries on so a graph sequence continues."""
+        pick = graphs if callable(graphs) else (lambda j: graphs[j % len(graphs)])
         with torch.cuda.stream(stream):
-            for i in range(warm):
-                graphs[i % len(graphs)].replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            pick(0).replay()
+            e1.record(stream)
             torch.cuda.synchronize()
+            n_warm = max(warm, int(min_warm_ms / max(e0.elapsed_time(e1), 1e-3)) + 1)
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(replays)]
-            torch.cuda._sleep(50_000_000)          # let the host queue the loop ahead of the GPU
+            for j in range(1, 1 + n_warm):
+                pick(j).replay()
             for i in range(replays):
                 ev[i][0].record(stream)
-                graphs[i % len(graphs)].replay()
+                pick(1 + n_warm + i).replay()
                 ev[i][1].record(stream)
         torch.cuda.synchronize()
         return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3 / per_replay
 
-    # the headline: exactly K steps (n_rep replays of d steps) after >= W warm-up steps, and at least
-    # two passes over every graph (the first replays after a capture run slower)
+    # the headline: exactly K steps (n_rep replays of d steps) after >= W warm-up steps, at least two
+    # passes over every graph and about 20 ms of warm-up work
     warm_rep = max(1, -(-args.warmup // d), 2 * len(starts))
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
@@ -475,8 +486,8 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
     wall = time.perf_counter() - t_wall0
     us_step = float(step_us.mean())
     # spread: 24 more replays of the same graphs (not part of the headline)
-    spread_us = timed(order if len(order) > 1 else [order[0]], 24, 1, d)
-    single_us = timed(g_single, max(K, 2 * R), 2 * R, 1)
+    spread_us = timed(order, 24, 1, d)
+    single_us = timed(g_single, max(K, 2 * R), 2 * R, 1)   # replay j is copy j mod R
     fc_us = timed([g_fc], 24, 2, FC_PER_GRAPH)
     kv_us = timed([g_kv], 24, 2, FC_PER_GRAPH)
     staged_us = timed([g_staged], 24, 1, 2 * R) if small else None
@@ -518,8 +529,8 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
         "ctx_len": ctx, "k_in": wl.geom.k_in, "hidden": wl.geom.hidden, "out_dim": wl.geom.out_dim,
         "layers": wl.geom.n_layers, "weight_copies": R, "step_bytes": alg["step_bytes"], "step_flops": alg["flops"],
         "timing": f"{K} steps timed as {n_rep} replay(s) of a captured graph of {d} consecutive steps, rotating "
-                  f"over {R} weight copies, HIP events around each replay on its stream, after {warm_rep * d} "
-                  "warm-up steps",
+                  f"over {R} weight copies, HIP events around each replay on its stream, right after at least "
+                  f"{warm_rep * d} warm-up steps (and about 20 ms of them) queued back to back",
         "steps": K, "steps_per_graph": d, "replays": n_rep,
         "us_per_step": round(us_step, 2),
         "rows_per_s": round(accepted / (us_step * 1e-6), 1),
