@@ -11,7 +11,13 @@
 //  * a workgroup of 4 waves (one per SIMD, one workgroup per CU) computes a
 //    256 (tokens) x 256 (features) tile; wave w takes all 256 tokens and
 //    features 64 w .. +64: an 8 x 2 grid of v_mfma_f32_32x32x16_bf16
-//    accumulators, 256 accumulation registers per lane;
+//    accumulators, 256 accumulation registers per lane.  When 256-token tiles
+//    would leave most CUs idle, tiles are 128 tokens tall (a 4 x 2 grid): a GEMM
+//    split over k to fill the chip then needs half the splits, and writes half
+//    the fp32 partials (at 1024 x 12288 x 4096: 2 splits and 32 MB instead of 4
+//    and 64 MB, the fc stage 108.5 -> 104.1 us; 4 splits of 128-token tiles, two
+//    workgroups per CU, took 109.8 us, and 128-token tiles at 4096 rows, two
+//    workgroups per CU, were slower than 256-token tiles, 345 against 328 us);
 //  * what bounds a GEMM on this chip, short of the matrix cores, is LDS
 //    bandwidth (measured: staging both operands of 64 x 128 wave tiles through
 //    LDS took 63% of such a kernel's time in loads and fragment reads).  Here
@@ -41,16 +47,14 @@
 
 namespace dfkv {
 
-constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int GBN = 256, GBK = 64;
 constexpr int GTHREADS = 256;                    // 4 waves, one per SIMD
-constexpr int GA_STAGE = GBM * GBK * 2;          // token tile of one stage in LDS: 32 KB
 constexpr int GCPR = GBK / 8;                    // 16-byte chunks per LDS row
-constexpr int GFM = GBM / 32, GFN = GBN / 4 / 32;
+constexpr int GFN = GBN / 4 / 32;
 constexpr int GNS = GBK / 16;                    // MFMA k slices per stage
-constexpr int GCPT = GBM * GCPR / GTHREADS;      // token-tile chunks per thread per stage (8)
 constexpr int GEP = GBN + 8;                     // fp32 row stride of the epilogue tile in LDS
 constexpr int GSLOTS = 4;                      // token-tile ring in LDS
-constexpr int GSMEM = GSLOTS * GA_STAGE > 64 * GEP * 4 ? GSLOTS * GA_STAGE : 64 * GEP * 4;
+constexpr int gemm_smem(int bm) { return GSLOTS * bm * GBK * 2 > 64 * GEP * 4 ? GSLOTS * bm * GBK * 2 : 64 * GEP * 4; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -61,9 +65,13 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // Wave w computes all 256 tokens x features w*64 .. +64.  k is permuted inside each 64-wide stage so
 // that a lane's weight fragment is 64 contiguous bytes: MFMA slice s, lane half h takes physical
 // k = 32 h + 8 s + (0..7), for both operands, which leaves every dot product unchanged.
-template <bool PACKED_W>
+template <bool PACKED_W, int GBM>
 __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t smem[GSMEM];
+    constexpr int GA_STAGE = GBM * GBK * 2;          // token tile of one stage in LDS: 32 KB (16 KB)
+    constexpr int GFM = GBM / 32;
+    constexpr int GCPT = GBM * GCPR / GTHREADS;      // token-tile chunks per thread per stage (8 or 4)
+    static_assert(GCPT == 8 || GCPT == 4, "the waits below are counted for 256- and 128-token tiles");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[gemm_smem(GBM)];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nx = (p.O + GBN - 1) / GBN, ny = (p.M + GBM - 1) / GBM;
@@ -157,10 +165,11 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
     // Per stage it each thread issues, in order: the weights of stage it+1, slices 0-2 (GFN loads
     // each, into the registers slice s of `it` has just used), the token tile of stage it+3 (GCPT),
     // the weights of stage it+1, slice 3.  Waiting for the weights of slice s of stage it (issued
-    // one stage earlier) leaves 14 later loads outstanding.  Between slices 2 and 3 sits the stage
-    // boundary: the token tile of it+1 (issued two stages earlier) has landed once at most 22 later
-    // loads are outstanding (24 in steady state; the first stage has 22, and waiting for 22 always
-    // only also waits for the weights of slice 3, issued a stage ago); the barrier makes every
+    // one stage earlier) leaves 6 + GCPT later loads outstanding (14 for 256-token tiles, 10 for
+    // 128).  Between slices 2 and 3 sits the stage boundary: the token tile of it+1 (issued two
+    // stages earlier) has landed once at most 14 + GCPT later loads are outstanding (16 + GCPT in
+    // steady state; the first stage has 14 + GCPT, and waiting for that many always only also
+    // waits for the weights of slice 3, issued a stage ago); the barrier makes every
     // wave's part visible and proves every wave done reading the slot of stage it-1 (its last
     // fragments were read during slice 2 of it-1 and used by slice 3), which then takes stage
     // it+3; slice 0 of it+1 is read while slice 3 of `it` multiplies.
@@ -170,7 +179,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
 #pragma unroll
         for (int s = 0; s < GNS; ++s) {
             if (s + 1 == GNS) {
-                asm volatile("s_waitcnt vmcnt(22)" ::: "memory");
+                if constexpr (GCPT == 8) asm volatile("s_waitcnt vmcnt(22)" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
                 __builtin_amdgcn_s_barrier();
                 issue_a(last(it + 3));
             }
@@ -178,7 +188,8 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
             // MFMAs of this one, into the other fragment set
             const uint8_t *rs = s + 1 < GNS ? sa : slot(it + 1);
             const int rsl = (s + 1) & (GNS - 1), rset = (s + 1) & 1;
-            asm volatile("s_waitcnt vmcnt(14)" : "+v"(bw[s][0]), "+v"(bw[s][1]));
+            if constexpr (GCPT == 8) asm volatile("s_waitcnt vmcnt(14)" : "+v"(bw[s][0]), "+v"(bw[s][1]));
+            else asm volatile("s_waitcnt vmcnt(10)" : "+v"(bw[s][0]), "+v"(bw[s][1]));
             __builtin_amdgcn_sched_barrier(0);
             // one fragment read after each of the first GFM MFMAs: the last read has the other half of
             // the slice's MFMAs to land in
@@ -200,15 +211,16 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
 
     if (it0 < it1) {
         // prologue: token tiles it0, it0+1; weights of it0, slices 0-2; token tile it0+2; weights of
-        // it0, slice 3 -- the steady-state order.  Tile it0 has landed once 24 later loads are
-        // outstanding.
+        // it0, slice 3 -- the steady-state order.  Tile it0 has landed once 8 + 2 GCPT later loads
+        // are outstanding.
         issue_a(it0);
         issue_a(last(it0 + 1));
 #pragma unroll
         for (int s = 0; s < GNS - 1; ++s) load_b(it0, s);
         issue_a(last(it0 + 2));
         load_b(it0, GNS - 1);
-        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+        if constexpr (GCPT == 8) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
         __builtin_amdgcn_s_barrier();
         read_a(slot(it0), 0, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -282,18 +294,26 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
     }
 }
 
-int gemm_tiles(int M, int O) { return ((O + GBN - 1) / GBN) * ((M + GBM - 1) / GBM); }
+// Token tile height: 128 when 256-token tiles would leave most CUs idle (fewer than 192 tiles),
+// which halves the k splits such a GEMM needs to fill the chip, and with them its fp32 partials.
+static int gemm_bm(int M, int O) { return ((O + GBN - 1) / GBN) * ((M + 255) / 256) < 192 ? 128 : 256; }
+
+int gemm_tiles(int M, int O) {
+    const int bm = gemm_bm(M, O);
+    return ((O + GBN - 1) / GBN) * ((M + bm - 1) / bm);
+}
 
 hipError_t launch_gemm(const GemmParams &p, hipStream_t s) {
     if (p.M <= 0) return hipSuccess;
     if (p.K % GBK != 0 || p.S < 1 || p.S > p.K / GBK || (p.S > 1 && !p.part) || (p.S == 1 && !p.part && !p.out))
         return hipErrorInvalidValue;
     const unsigned tiles = (unsigned)gemm_tiles(p.M, p.O);
+    const bool small = gemm_bm(p.M, p.O) == 128;
     if (p.w_packed) {
         if (p.O % 64 != 0) return hipErrorInvalidValue;
-        return launch1(k_gemm<true>, dim3(tiles * (unsigned)p.S), dim3(GTHREADS), s, p);
+        return launch1(small ? k_gemm<true, 128> : k_gemm<true, 256>, dim3(tiles * (unsigned)p.S), dim3(GTHREADS), s, p);
     }
-    return launch1(k_gemm<false>, dim3(tiles * (unsigned)p.S), dim3(GTHREADS), s, p);
+    return launch1(small ? k_gemm<false, 128> : k_gemm<false, 256>, dim3(tiles * (unsigned)p.S), dim3(GTHREADS), s, p);
 }
 
 }  // namespace dfkv
