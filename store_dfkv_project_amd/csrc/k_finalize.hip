@@ -228,19 +228,23 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
         l = (int)(((float)cc + 0.5f) * inv_lch);
         rem = cc - l * lch;
     };
+    // In place (the rows are read from kv_out and written back there), a V chunk is already final:
+    // it is only read when the row goes to the pool, and never written back.
+    const bool inplace = !p.part && p.kv_out && p.src == p.kv_out;
     u32x4 y[kFinVPer];
-    auto load_group = [&](int base) {
+    // chunks c0 <= c < c1 of the group at base (the others of the group are left as they are)
+    auto load_group = [&](int base, int c0, int c1) {
 #pragma unroll
         for (int m = 0; m < kFinVPer; ++m) {
             const int c = base + m * kFinVThreads + tid;
             bool isk;
             int l, rem;
             split(c, isk, l, rem);
-            y[m] = c < nch ? load_y8(p, row, (int64_t)l * p.per_layer + (isk ? 0 : p.nkv * HD) + rem * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
+            if (c >= c0) y[m] = c < c1 ? load_y8(p, row, (int64_t)l * p.per_layer + (isk ? 0 : p.nkv * HD) + rem * 8)
+                                       : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    load_group(0);
+    load_group(0, 0, inplace ? kch : nch);
 
     // the row's cos/sin values (rope_dim = HD floats) and the k_norm weights of every layer
     const float *cs = rope_row(p.nr, row);
@@ -262,13 +266,16 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
     const int64_t dst0 = w ? slot_offset(p, slot) : 0;
     uint16_t *const out_row = p.kv_out ? p.kv_out + (int64_t)row * p.O : nullptr;
     const float inv_hd = 1.0f / (float)HD;   // exact: HD is a power of two
+    // the chunks this row needs: in place, those past the K part only when the row is stored
+    const int cend = inplace && !w ? kch : nch;
+    if (inplace && w) load_group(0, kch, nch);
     __syncthreads();
 
     for (int base = 0;;) {
 #pragma unroll
         for (int m = 0; m < kFinVPer; ++m) {
             const int c = base + m * kFinVThreads + tid;
-            const bool ok = c < nch;
+            const bool ok = c < cend;
             bool isk;
             int l, rem;
             split(c, isk, l, rem);
@@ -323,12 +330,12 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
             }
             if (!ok) continue;
             const int64_t col = (int64_t)l * p.per_layer + (isk ? 0 : p.nkv * HD) + rem * 8;
-            if (out_row) *(u32x4 *)(out_row + col) = o;
+            if (out_row && (isk || !inplace)) *(u32x4 *)(out_row + col) = o;
             if (w) *(u32x4 *)((isk ? p.pk[l] : p.pv[l]) + dst0 + (int64_t)h * p.sh + q * 8) = o;
         }
         base += kFinVThreads * kFinVPer;
-        if (base >= nch) break;
-        load_group(base);
+        if (base >= cend) break;
+        load_group(base, base, cend);
     }
 }
 
