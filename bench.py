@@ -16,7 +16,7 @@ consecutive steps (d = the smallest divisor of --steps that is at least 8, else
 after the 3 others, and 4 x the weight bytes exceed the 256 MiB Infinity Cache,
 so every step streams its weights from HBM; the graphs continue the rotation
 across replay boundaries).  HIP events bracket every replay on its stream; the
-warm-up replays (at least --warmup steps and about 20 ms of work, so the clocks
+warm-up replays (at least --warmup steps and about 200 ms of work, so the clocks
 have settled) are queued right before the timed ones with no synchronisation
 between, so the GPU never waits for the host.  A step sits
 inside the serving loop's own graph, so a per-step graph launch is excluded
@@ -451,7 +451,7 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
     torch.cuda.synchronize()
     accepted = int(ds.write_mask.sum().item())
 
-    def timed(graphs, replays, warm, per_replay, min_warm_ms=20.0):
+    def timed(graphs, replays, warm, per_replay, min_warm_ms=200.0):
         """HIP events around every replay on the replay stream; returns per-unit us (replay / per_replay).
         `graphs`: a list, cycled, or a function of the replay's index.  The warm-up replays (at least
         `warm`, and about min_warm_ms of GPU work, so that the clocks have settled) run back to back
@@ -477,7 +477,7 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
         return np.array([a.elapsed_time(b) for a, b in ev]) * 1e3 / per_replay
 
     # the headline: exactly K steps (n_rep replays of d steps) after >= W warm-up steps, at least two
-    # passes over every graph and about 20 ms of warm-up work
+    # passes over every graph and about 200 ms of warm-up work
     warm_rep = max(1, -(-args.warmup // d), 2 * len(starts))
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
@@ -530,7 +530,7 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
         "layers": wl.geom.n_layers, "weight_copies": R, "step_bytes": alg["step_bytes"], "step_flops": alg["flops"],
         "timing": f"{K} steps timed as {n_rep} replay(s) of a captured graph of {d} consecutive steps, rotating "
                   f"over {R} weight copies, HIP events around each replay on its stream, right after at least "
-                  f"{warm_rep * d} warm-up steps (and about 20 ms of them) queued back to back",
+                  f"{warm_rep * d} warm-up steps (and about 200 ms of them) queued back to back",
         "steps": K, "steps_per_graph": d, "replays": n_rep,
         "us_per_step": round(us_step, 2),
         "rows_per_s": round(accepted / (us_step * 1e-6), 1),
