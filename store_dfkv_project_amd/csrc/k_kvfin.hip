@@ -48,6 +48,7 @@ constexpr int kKvThreads = kKvWaves * 64;
 #endif
 constexpr int kKvRing = DFKV_KV_RING;
 constexpr int kKvWPE = DFKV_KV_WPE;
+constexpr int kKvStatMax = 8;   // row statistics per lane held in registers (hidden <= 8192)
 
 // Row and request bookkeeping group 0 leaves in the workspace for the finalize kernel.
 __device__ __forceinline__ int64_t *book_slot(void *b) { return (int64_t *)b; }
@@ -331,11 +332,31 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
         }
         if (row_lane && fin.store && fin.row_valid) rv = fin.row_valid[tid];
     }
-    for (int n = wave; n < M; n += WAVES) {  // rinv[n] = 1/sqrt(mean(f[n]^2) + eps), fixed order
+    // rinv[n] = 1/sqrt(mean(f[n]^2) + eps), fixed order: lane l adds tt = l, l + 64, ... of row n.
+    // With at most 8 rows and T_in <= 64 * kKvStatMax, wave w takes row w and loads its statistics
+    // in one round (a loop that waited load by load put four to seven dependent round trips behind
+    // the ring); otherwise the loop.
+    if (M <= WAVES && p.T_in <= 64 * kKvStatMax) {
+        const int n_ld = wave < M ? wave : M - 1;
+        float sst[kKvStatMax];
+#pragma unroll
+        for (int i = 0; i < kKvStatMax; ++i) {
+            const int tt = lane + 64 * i;
+            sst[i] = p.ss_in[(int64_t)(tt < p.T_in ? tt : p.T_in - 1) * M + n_ld];
+        }
         float ss = 0.f;
-        for (int tt = lane; tt < p.T_in; tt += 64) ss += p.ss_in[(int64_t)tt * M + n];
+#pragma unroll
+        for (int i = 0; i < kKvStatMax; ++i)
+            if (lane + 64 * i < p.T_in) ss += sst[i];
         ss = wave_sum(ss);
-        if (lane == 0) sh_rinv[n] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+        if (lane == 0 && wave < M) sh_rinv[wave] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+    } else {
+        for (int n = wave; n < M; n += WAVES) {
+            float ss = 0.f;
+            for (int tt = lane; tt < p.T_in; tt += 64) ss += p.ss_in[(int64_t)tt * M + n];
+            ss = wave_sum(ss);
+            if (lane == 0) sh_rinv[n] = 1.0f / sqrtf(ss / (float)p.K + p.eps);
+        }
     }
     __syncthreads();
 #pragma unroll
