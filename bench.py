@@ -16,7 +16,7 @@ consecutive steps (d = the smallest divisor of --steps that is at least 8, else
 after the 3 others, and 4 x the weight bytes exceed the 256 MiB Infinity Cache,
 so every step streams its weights from HBM; the graphs continue the rotation
 across replay boundaries).  HIP events bracket every replay on its stream; the
-warm-up replays (at least --warmup steps and about 200 ms of work, so the clocks
+warm-up replays (at least --warmup steps and --warm-ms of work, 200 ms by default, so the clocks
 have settled) are queued right before the timed ones with no synchronisation
 between, so the GPU never waits for the host.  A step sits
 inside the serving loop's own graph, so a per-step graph launch is excluded
@@ -451,12 +451,14 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
     torch.cuda.synchronize()
     accepted = int(ds.write_mask.sum().item())
 
-    def timed(graphs, replays, warm, per_replay, min_warm_ms=200.0):
+    def timed(graphs, replays, warm, per_replay, min_warm_ms=None):
         """HIP events around every replay on the replay stream; returns per-unit us (replay / per_replay).
         `graphs`: a list, cycled, or a function of the replay's index.  The warm-up replays (at least
         `warm`, and about min_warm_ms of GPU work, so that the clocks have settled) run back to back
         right before the timed ones, with no synchronisation between: the GPU stays busy while the host
         queues the timed replays, and the replay index carries on so a graph sequence continues."""
+        if min_warm_ms is None:
+            min_warm_ms = args.warm_ms
         pick = graphs if callable(graphs) else (lambda j: graphs[j % len(graphs)])
         with torch.cuda.stream(stream):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -530,7 +532,7 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
         "layers": wl.geom.n_layers, "weight_copies": R, "step_bytes": alg["step_bytes"], "step_flops": alg["flops"],
         "timing": f"{K} steps timed as {n_rep} replay(s) of a captured graph of {d} consecutive steps, rotating "
                   f"over {R} weight copies, HIP events around each replay on its stream, right after at least "
-                  f"{warm_rep * d} warm-up steps (and about 200 ms of them) queued back to back",
+                  f"{warm_rep * d} warm-up steps (and about {args.warm_ms:g} ms of them) queued back to back",
         "steps": K, "steps_per_graph": d, "replays": n_rep,
         "us_per_step": round(us_step, 2),
         "rows_per_s": round(accepted / (us_step * 1e-6), 1),
@@ -571,6 +573,9 @@ def main() -> int:
                                                               "headline, then 2)")
     ap.add_argument("--ctx", type=int, default=None, help="context length of the bs=1 workloads")
     ap.add_argument("--copies", type=int, default=4, help="weight copies rotated through (cache defeat)")
+    ap.add_argument("--warm-ms", type=float, default=200.0,
+                    help="untimed warm-up before every timed series, in ms of GPU work (besides --warmup steps); "
+                         "a profiler run can lower it to keep its trace small")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-overlap", action="store_true", help="skip the overlapped-projection measurement")
