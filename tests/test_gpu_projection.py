@@ -182,7 +182,14 @@ def test_norm_rope_far_positions(orc, kind):
     ds.norm_rope(ds.kv_out)
     torch.cuda.synchronize()
     want = orc.norm_rope(geom, y, wl.w_knorm, wl.ctx_len, orc.rope_cache(rope, wl.cache_len))
-    assert_close_bf16(ds.bits(ds.kv_out), want, "norm_rope far positions")
+    got = ds.bits(ds.kv_out)
+    assert_close_bf16(got, want, "norm_rope far positions")
+    if kind == GQA:
+        # V heads are untouched: every V element keeps its input bits
+        kv = geom.n_kv_heads * geom.head_dim
+        for l in range(geom.n_layers):
+            v0 = l * geom.per_layer + kv
+            assert np.array_equal(got.reshape(ds.N, -1)[:, v0:v0 + kv], y.reshape(ds.N, -1)[:, v0:v0 + kv]), l
 
 
 @pytest.mark.parametrize("geom,B", [(GQA_W1, 40), (GQA_G, 30)], ids=["gqaW640-B40", "gqa128-B30"])
