@@ -118,6 +118,7 @@ def test_project_matches_oracle(orc, name, geom, B, rope):
     torch.cuda.synchronize()
     assert_close_bf16(ds.bits(ds.kv_out), ref["y"], f"{name} y")
     # standalone k_norm + RoPE on the GPU's y
+    y_gpu_in = ds.kv_out.clone()
     y_gpu = ds.kv_out.clone()
     ds.norm_rope(y_gpu)
     torch.cuda.synchronize()
@@ -128,6 +129,13 @@ def test_project_matches_oracle(orc, name, geom, B, rope):
     ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
     torch.cuda.synchronize()
     stats = assert_close_bf16(ds.bits(ds.kv_out), ref["kv"], f"{name} kv")
+    if geom.kind == GQA:
+        # V has no norm and no rotation: the fused V halves are the unfused projection's, bit for bit
+        got, y_bits = ds.bits(ds.kv_out).reshape(ds.N, -1), ds.bits(y_gpu_in).reshape(ds.N, -1)
+        kv = geom.n_kv_heads * geom.head_dim
+        for l in range(geom.n_layers):
+            v0 = l * geom.per_layer + kv
+            assert np.array_equal(got[:, v0:v0 + kv], y_bits[:, v0:v0 + kv]), f"{name} layer {l} V"
     # deterministic: a second call gives the same bits
     first = ds.kv_out.clone()
     ds.project(flags=dfkv.DFKV_FUSE_NORM_ROPE)
