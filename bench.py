@@ -55,7 +55,10 @@ BF16_PEAK_TFLOPS = 2500.0
 
 # copy-calibrated FETCH_SIZE + WRITE_SIZE of the dominant (fc) stage, per workload the counters were taken on
 TRAFFIC_FILES = {1: os.path.join(ROOT, "profiles", "k_stream_fc_dense_bs1_hbm_counters.md"),
-                 2: os.path.join(ROOT, "profiles", "k_gemm_dense_bs64_hbm_counters.md")}
+                 2: os.path.join(ROOT, "profiles", "k_gemm_dense_bs64_hbm_counters.md"),
+                 3: os.path.join(ROOT, "profiles", "k_stream_fc_mla_bs1_hbm_counters.md")}
+# the context lengths the small-batch counters were taken at (the bench's default for each workload)
+TRAFFIC_CTX = {1: 32768, 3: 2048}
 
 
 def source_digest() -> str:
@@ -499,8 +502,8 @@ def run_workload(cfg: int, ctx, args, extras: bool) -> dict:
     kv_mean = float(kv_us.mean())
     if wl.n_rows <= 64:
         achieved = alg["fc_bytes"] / (fc_mean * 1e-6) / 1e9
-        # the counters were taken on the bs=1 dense workload at 32768 context; other workloads report null
-        traffic = measured_traffic(cfg) if cfg == 1 and ctx == 32768 else None
+        # counters exist for the dense and MLA bs=1 workloads at their default context; others report null
+        traffic = measured_traffic(cfg) if TRAFFIC_CTX.get(cfg) == ctx else None
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBS, 4), traffic=traffic,
                     kernel="k_stream<fc> (dfkv_project_fc: the fc GEMM streaming the tiled w_fc, f + row statistics)",

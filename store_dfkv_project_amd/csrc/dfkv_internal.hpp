@@ -16,6 +16,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// 16 bytes of a weight that a step streams exactly once (the weight-streaming GEMMs at small batch),
+// loaded non-temporally: the stream then does not evict what the step reads again from the caches
+// (the next kernels' code and arguments, the fc output, the split partials).  Measured on MI355X:
+// dense drafter at 4 rows 40.6 -> 38.5 us per step, MLA drafter at 4 rows 66.0 -> 60.5 us.
+__device__ __forceinline__ u32x4 load_streamed(const uint16_t *p) {
+    return __builtin_nontemporal_load((const u32x4 *)p);
+}
+
 // bf16 bits -> fp32 (exact)
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

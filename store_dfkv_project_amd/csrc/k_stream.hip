@@ -1,7 +1,7 @@
 // k_stream.hip -- the weight-streaming GEMMs of the two-kernel projection at
 // small batch (M = B*W <= 64 token rows): fc (f and its row statistics) and the
 // stacked K/V GEMM (fp32 split partials), one launch each.  The per-workgroup
-// work lives in stream_core.hpp, shared with the one-launch step.
+// work lives in stream_core.hpp.
 #include "stream_core.hpp"
 
 namespace dfkv {

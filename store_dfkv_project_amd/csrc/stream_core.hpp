@@ -68,7 +68,7 @@ __device__ __forceinline__ void stream_tile(const StreamParams &p, int t, int s,
         const int64_t kb = kb0 + wave + j * WAVES, k = kb * 128;
         const uint16_t *wp = wpiece(kb);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a[slot][u] = *(const u32x4 *)(wp + u * w_u);
+        for (int u = 0; u < 4; ++u) a[slot][u] = load_streamed(wp + u * w_u);
         if (!STAGE) {
 #pragma unroll
             for (int ng = 0; ng < NG; ++ng) {
