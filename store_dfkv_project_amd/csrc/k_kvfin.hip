@@ -38,15 +38,10 @@ namespace dfkv {
 
 constexpr int kKvWaves = 8;
 constexpr int kKvThreads = kKvWaves * 64;
-// Tuning (overridable when building): weight k-blocks in flight per wave, and waves per SIMD
-// (4: <= 128 VGPRs, two workgroups per CU).
-#ifndef DFKV_KV_RING
-#define DFKV_KV_RING 3
-#endif
+// Waves per SIMD of k_kvgroups (4: <= 128 VGPRs, two workgroups per CU; overridable when building).
 #ifndef DFKV_KV_WPE
 #define DFKV_KV_WPE 4
 #endif
-constexpr int kKvRing = DFKV_KV_RING;
 constexpr int kKvWPE = DFKV_KV_WPE;
 constexpr int kKvStatMax = 8;   // row statistics per lane held in registers (hidden <= 8192)
 
@@ -264,9 +259,13 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
 // The staging hop's loads are issued before the weight ring, so that g is ready while the ring is in
 // flight (measured on MI355X against the ring first: MLA drafter at 4 rows, K/V stage 0.65 us
 // shorter; dense drafter at 4 rows, step 0.2 us shorter).
+// D: weight k-blocks in flight per wave.  With two groups per CU one is enough -- 16 waves keep
+// 64 KB per CU in flight, and a deeper ring only queues in front of the other group's staging hop
+// (measured: dense drafter at 4 rows, 38.1 us per step with 3, 37.5 with 2, 37.4 with 1); with one
+// group per CU two (MLA drafter at 4 rows, K/V stage 11.5 us with 2 or 3, 11.8 with 1).
+template <int D>
 __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvWPE, 8))) void k_kvgroups(
     const KvParams kp) {
-    constexpr int D = kKvRing;
     constexpr int WAVES = kKvWaves, NT = kKvThreads, NP = 17;
     __shared__ float red[2 * kKvWaves * 16 * 17];
     __shared__ float sh_rinv[16];
@@ -491,7 +490,9 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
         return hipErrorInvalidValue;
     const size_t M = (size_t)p.kv.M;
     const size_t g_bytes = M * (size_t)(p.kv.nbs * 128 + 8) * 2;
-    hipError_t e = launch1(k_kvgroups, dim3((unsigned)p.n_groups), dim3(kKvThreads), s, p, g_bytes);
+    const bool two_per_cu = p.n_groups > kKvSlots / 2;
+    hipError_t e = launch1(two_per_cu ? k_kvgroups<1> : k_kvgroups<2>, dim3((unsigned)p.n_groups), dim3(kKvThreads),
+                           s, p, g_bytes);
     if (e != hipSuccess) return e;
     // finalize: rows per workgroup such that the unit's partials are one round of loads (2 per
     // thread) and each row has its own wave; LDS: the rows [rows][unit_cols] bf16, the k_norm
