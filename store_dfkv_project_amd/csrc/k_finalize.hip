@@ -211,12 +211,22 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
     // chunk with +sin (k = u c + u' s', u' the partner's normalised value)
     __shared__ __attribute__((aligned(16))) float s_cs[HD + half];
     __shared__ __attribute__((aligned(16))) uint16_t s_wk[DFKV_MAX_LAYERS * HD];      // [L][HD]
+    // the kernel arguments of the row's path in one round of scalar loads: a field read where the
+    // code first needs it is a round trip of its own through the scalar cache, which starts cold in
+    // every kernel (the fields the first arithmetic uses pass through the statement, so that it
+    // cannot start before it)
+    int W = p.W, nkv = p.nkv, L = p.L;
+    asm volatile("" : "+s"(W), "+s"(nkv), "+s"(L) : "s"(p.part), "s"(p.src), "s"(p.kv_out), "s"(p.S), "s"(p.M),
+                 "s"(p.O), "s"(p.per_layer), "s"(p.store), "s"(p.advance), "s"(p.nr.cos_sin), "s"(p.nr.cache_len),
+                 "s"(p.nr.ctx_len_in), "s"(p.nr.width), "s"(p.nr.rope_dim), "s"(p.nr.w_knorm), "s"(p.nr.eps),
+                 "s"(p.dummy), "s"(p.n_acc), "s"(p.ctx_len), "s"(p.limit), "s"(p.row_valid), "s"(p.bt),
+                 "s"(p.bt_stride), "s"(p.bt_cols), "s"(p.num_pages), "s"(p.pg));
     const int row = blockIdx.x;
-    const int r = row / p.W, i = row - (row / p.W) * p.W;
+    const int r = row / W, i = row - (row / W) * W;
     const int tid = threadIdx.x;
 
-    const int lch = p.nkv * qh;             // K (or V) chunks of one layer
-    const int kch = p.L * lch;              // K chunks of the row; as many V chunks follow
+    const int lch = nkv * qh;               // K (or V) chunks of one layer
+    const int kch = L * lch;                // K chunks of the row; as many V chunks follow
     const int nch = 2 * kch;
     // chunk c -> (K or V, layer l, offset rem in the layer's K or V part); cc / lch by a float
     // reciprocal: cc / lch <= 2 * layers <= 64, so the product is within 4e-6 of the quotient while

@@ -66,13 +66,19 @@ __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 // that a lane's weight fragment is 64 contiguous bytes: MFMA slice s, lane half h takes physical
 // k = 32 h + 8 s + (0..7), for both operands, which leaves every dot product unchanged.
 template <bool PACKED_W, int GBM>
-__global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams p) {
+__global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams pin) {
     constexpr int GA_STAGE = GBM * GBK * 2;          // token tile of one stage in LDS: 32 KB (16 KB)
     constexpr int GFM = GBM / 32;
     constexpr int GCPT = GBM * GCPR / GTHREADS;      // token-tile chunks per thread per stage (8 or 4)
     static_assert(GCPT == 8 || GCPT == 4, "the waits below are counted for 256- and 128-token tiles");
     __shared__ __attribute__((aligned(16))) uint8_t smem[gemm_smem(GBM)];
 
+    // the kernel arguments in one round of scalar loads: a field read where the code first needs it
+    // is a round trip of its own through the scalar cache, which starts cold in every kernel (the
+    // sizes pass through the statement, so that no arithmetic on them starts before it)
+    GemmParams p = pin;
+    asm volatile("" : "+s"(p.M), "+s"(p.K), "+s"(p.O), "+s"(p.S) : "s"(p.x), "s"(p.ldx), "s"(p.w), "s"(p.out),
+                 "s"(p.ldo), "s"(p.part));
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nx = (p.O + GBN - 1) / GBN, ny = (p.M + GBM - 1) / GBM;
     const int tiles = nx * ny;

@@ -57,9 +57,12 @@ struct WCfg {
 // physical k = 32 h + 8 s + (0..7) of both operands, so a lane's token fragment over a stage is 64
 // contiguous bytes and every dot product is unchanged.
 template <int FM, bool PACKED>
-__global__ __launch_bounds__(WTHREADS, 1) void k_gemm_w(const GemmParams p) {
+__global__ __launch_bounds__(WTHREADS, 1) void k_gemm_w(const GemmParams pin) {
     using C = WCfg<FM>;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::SMEM];
+    // the kernel arguments in one round of scalar loads (see k_gemm)
+    GemmParams p = pin;
+    asm volatile("" : "+s"(p.M), "+s"(p.K), "+s"(p.O) : "s"(p.x), "s"(p.ldx), "s"(p.w), "s"(p.out), "s"(p.ldo));
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nx = p.O / C::XR, ny = (p.M + WBM - 1) / WBM;

@@ -83,7 +83,12 @@ constexpr int kHnpThreads = 512;
 constexpr int kHnpLds = 128 * 1024;   // the larger of the two LDS sizes (R * H * 2 bytes fit in it)
 
 template <int LDS>
-__global__ __launch_bounds__(kHnpThreads) void k_hidden_norm_packed(const HiddenNormArgs a) {
+__global__ __launch_bounds__(kHnpThreads) void k_hidden_norm_packed(const HiddenNormArgs ain) {
+    // the kernel arguments in one round of scalar loads: a field read where the code first needs it
+    // is a round trip of its own through the scalar cache, which starts cold in every kernel
+    HiddenNormArgs a = ain;
+    asm volatile("" : "+s"(a.packed), "+s"(a.H), "+s"(a.S), "+s"(a.n_rows) : "s"(a.w), "s"(a.f), "s"(a.g), "s"(a.part),
+                 "s"(a.eps));
     __shared__ __attribute__((aligned(16))) uint8_t hn_lds[LDS];
     uint16_t *rows = (uint16_t *)hn_lds;                // [R][H] bf16
     __shared__ float ssp[8], rinv_s[4];

@@ -15,6 +15,11 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WPE,
     __shared__ float red[stream_red_floats<NG, WAVES>()];
     __shared__ float sh_rinv[16];
     extern __shared__ __attribute__((aligned(16))) uint16_t sh_g[];  // STAGE: [M][kc + 8]
+    // the kernel arguments in one round of scalar loads: a field read where the code first needs it
+    // is a round trip of its own through the scalar cache, which starts cold in every kernel
+    asm volatile("" ::"s"(p.S), "s"(p.M), "s"(p.K), "s"(p.O), "s"(p.nbs), "s"(p.w), "s"(p.w_tiled), "s"(p.x),
+                 "s"(p.ldx), "s"(p.out), "s"(p.ss_out), "s"(p.part));
+    if constexpr (STAGE) asm volatile("" ::"s"(p.w_hn), "s"(p.ss_in), "s"(p.T_in), "s"(p.eps));
     const int t = blockIdx.x / p.S, s = blockIdx.x - (blockIdx.x / p.S) * p.S;
     stream_tile<NG, WAVES, D, STAGE>(p, t, s, red, sh_g, sh_rinv);
 }
