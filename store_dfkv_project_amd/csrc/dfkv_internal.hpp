@@ -16,6 +16,12 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// a / b for integers 0 <= a < 2^21 and b >= 1, given rb = 1 / b in fp32: the fp32 product of a + 0.5
+// and rb is within 2^-22 relative of (a + 0.5) / b, whose fraction part is at least 0.5 / b away from
+// an integer, so truncation gives floor(a / b) exactly -- a few instructions where a 32-bit integer
+// division by a value known only at run time takes about thirty, on the path to a kernel's first loads.
+__device__ __forceinline__ int div_small(int a, float rb) { return (int)(((float)a + 0.5f) * rb); }
+
 // 16 bytes of a weight that a step streams exactly once (the weight-streaming GEMMs at small batch),
 // loaded non-temporally: the stream then does not evict what the step reads again from the caches
 // (the next kernels' code and arguments, the fc output, the split partials).  Measured on MI355X:
@@ -215,6 +221,7 @@ struct KvParams {
     FinalizeParams fin;       // k_norm/RoPE, store, advance
     void *book;               // bookkeeping area of the workspace
     int32_t n_groups;         // kv.S splits x (O/16/ntg) tile groups
+    int32_t groups;           // tile groups per split, n_groups / kv.S (set by launch_kv)
     int32_t ntg;              // tiles per group
     int32_t unit_cols;        // output columns per unit (head_dim for GQA, latent + rope for MLA)
     int32_t n_units;          // O / unit_cols

@@ -222,7 +222,7 @@ __global__ __launch_bounds__(kFinVThreads) void k_finalize_gqa(const FinalizePar
                  "s"(p.dummy), "s"(p.n_acc), "s"(p.ctx_len), "s"(p.limit), "s"(p.row_valid), "s"(p.bt),
                  "s"(p.bt_stride), "s"(p.bt_cols), "s"(p.num_pages), "s"(p.pg));
     const int row = blockIdx.x;
-    const int r = row / W, i = row - (row / W) * W;
+    const int r = div_small(row, 1.0f / (float)W), i = row - r * W;   // (row < 2^21)
     const int tid = threadIdx.x;
 
     const int lch = nkv * qh;               // K (or V) chunks of one layer

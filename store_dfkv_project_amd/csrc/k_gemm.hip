@@ -82,20 +82,22 @@ __global__ __launch_bounds__(GTHREADS, 1) void k_gemm(const GemmParams pin) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int nx = (p.O + GBN - 1) / GBN, ny = (p.M + GBM - 1) / GBM;
     const int tiles = nx * ny;
-    const int split = blockIdx.x / tiles;
-    int t = blockIdx.x % tiles;
+    // the divisions by values known only at run time by div_small (every operand is below 2^21)
+    const int split = div_small((int)blockIdx.x, 1.0f / (float)tiles);
+    int t = (int)blockIdx.x - split * tiles;
     // XCD-aware order: when the tile count divides by 8, the tiles of XCD x (workgroups b with
     // b % 8 == x) become the consecutive logical tiles x*tiles/8 .. +tiles/8
     if (tiles % 8 == 0) t = (t % 8) * (tiles / 8) + t / 8;
     // logical tile -> (tm, tn) in bands of up to 4 token tiles, feature-major inside a band
     const int band = ny < 4 ? ny : 4;
     const int per_band = band * nx;
-    const int b0 = t / per_band, in_b = t % per_band;
+    const int b0 = div_small(t, 1.0f / (float)per_band), in_b = t - b0 * per_band;
     const int rows_b = (b0 + 1) * band <= ny ? band : ny - b0 * band;
-    const int tm = b0 * band + in_b % rows_b, tn = in_b / rows_b;
+    const int tn = div_small(in_b, 1.0f / (float)rows_b), tm = b0 * band + in_b - tn * rows_b;
     const int m0 = tm * GBM, o0 = tn * GBN;
     const int iters = p.K / GBK;
-    const int it0 = (int)((int64_t)split * iters / p.S), it1 = (int)((int64_t)(split + 1) * iters / p.S);
+    const float rS = 1.0f / (float)p.S;
+    const int it0 = div_small(split * iters, rS), it1 = div_small((split + 1) * iters, rS);
     const int fr = lane & 31, fh = lane >> 5;
 
     // token tile: this thread's chunks, chunk L = (i*4 + wave)*64 + lane -> row L/8, LDS position

@@ -74,9 +74,9 @@ __global__ __launch_bounds__(WTHREADS, 1) void k_gemm_w(const GemmParams pin) {
     // logical tile -> (tm, tn) in bands of up to 4 token tiles, feature-major inside a band
     const int band = ny < 4 ? ny : 4;
     const int per_band = band * nx;
-    const int b0 = t / per_band, in_b = t % per_band;
+    const int b0 = div_small(t, 1.0f / (float)per_band), in_b = t - b0 * per_band;   // (operands < 2^21)
     const int rows_b = (b0 + 1) * band <= ny ? band : ny - b0 * band;
-    const int tm = b0 * band + in_b % rows_b, tn = in_b / rows_b;
+    const int tn = div_small(in_b, 1.0f / (float)rows_b), tm = b0 * band + in_b - tn * rows_b;
     const int n0 = tm * WBM, o0 = tn * C::XR;
     const int it0 = 0, it1 = p.K / WBK;
     const int fr = lane & 31, fh = lane >> 5;

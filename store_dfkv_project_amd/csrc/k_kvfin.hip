@@ -101,25 +101,26 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     // own before the first data load (eight here).  Naming the fields the unit path needs in empty asm
     // statements makes them live in scalar registers at this point, so that their loads go out
     // together with one wait (measured on MI355X: 0.35 us per step, dense drafter at 4 rows).
-    asm volatile("" ::"s"(p.M), "s"(kp.fin_rows), "s"(kp.n_units), "s"(p.O), "s"(p.S), "s"(kp.unit_cols),
+    asm volatile("" ::"s"(p.M), "s"(kp.fin_rows), "s"(p.L), "s"(p.O), "s"(p.S), "s"(kp.unit_cols),
                  "s"(p.kind), "s"(p.nkv), "s"(p.per_layer), "s"(p.norm), "s"(p.nr.rope_dim), "s"(p.nr.latent),
                  "s"(kp.lds_wk), "s"(kp.lds_cs), "s"(p.store), "s"(p.pg));
     asm volatile("" ::"s"(kp.book), "s"(p.nr.w_knorm), "s"(p.part), "s"(p.kv_out), "s"(p.sp), "s"(p.ss), "s"(p.sh),
                  "s"(p.nr.eps));
-    const int nrb = (p.M + kp.fin_rows - 1) / kp.fin_rows;
-    if ((int)blockIdx.x == kp.n_units * nrb) {   // the last workgroup: the bookkeeping outputs
-        kvfinal_bookkeeping(p, kp.book);
+    // grid (row block, unit of the layer, layer), plus the slice z = L whose first workgroup writes the
+    // bookkeeping outputs (the others of that slice have nothing to do)
+    if ((int)blockIdx.z == p.L) {
+        if (blockIdx.x == 0 && blockIdx.y == 0) kvfinal_bookkeeping(p, kp.book);
         return;
     }
-    const int u = blockIdx.x / nrb, rb = blockIdx.x - (blockIdx.x / nrb) * nrb;
+    const bool gqa = p.kind == DFKV_GQA;
+    const int u = gqa ? (int)blockIdx.z * 2 * p.nkv + (int)blockIdx.y : (int)blockIdx.z, rb = (int)blockIdx.x;
     const int n0 = rb * kp.fin_rows;
     const int M = p.M - n0 < kp.fin_rows ? p.M - n0 : kp.fin_rows;  // rows of this workgroup
     const int Mall = p.M, O = p.O, S = p.S;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int cols = kp.unit_cols;
-    const bool gqa = p.kind == DFKV_GQA;
-    const int l = gqa ? u / (2 * p.nkv) : u;
-    const int rem = gqa ? u - l * 2 * p.nkv : 0;
+    const int l = (int)blockIdx.z;
+    const int rem = gqa ? (int)blockIdx.y : 0;
     const bool is_v = gqa && rem >= p.nkv;
     const int h = is_v ? rem - p.nkv : rem;
     const int64_t col0 = gqa ? (int64_t)u * cols : (int64_t)l * p.per_layer;
@@ -141,6 +142,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     constexpr int WKN = 1024 / kKvThreads;               // k_norm weights per thread (nwk <= 1024)
     constexpr int CSF = kKvWaves * 256 / kKvThreads;     // cos/sin values per thread (<= 8 rows x 256)
     const int total = M * cols;
+    const float rcols = 1.0f / (float)cols;
     uint16_t wkv[WKN];
     float csv[CSF];
     const uint16_t *wsrc = p.nr.w_knorm + (int64_t)l * nwk;
@@ -163,7 +165,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
 #pragma unroll
             for (int i = 0; i < EB; ++i) {
                 const int e = e0 + i * kKvThreads;
-                const int n = e / cols, c = e - (e / cols) * cols;
+                const int n = div_small(e, rcols), c = e - n * cols;
 #pragma unroll
                 for (int k = 0; k < SB; ++k)
                     v[i][k] = (e < total && s0 + k < S) ? p.part[((int64_t)(s0 + k) * Mall + n0 + n) * O + col0 + c]
@@ -282,22 +284,21 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     extern __shared__ __attribute__((aligned(16))) uint16_t sh_g[];  // g [M][kc + 8]
     const StreamParams &p = kp.kv;
     const FinalizeParams &fin = kp.fin;
-    // the kernel arguments of the main path in one round of scalar loads (see k_kvfinal); the group
-    // and split counts pass through the statement so that no arithmetic on them starts before it
-    int n_groups = kp.n_groups, n_splits = p.S;
-    asm volatile("" : "+s"(n_groups), "+s"(n_splits) : "s"(kp.ntg), "s"(p.M), "s"(p.nbs), "s"(p.K), "s"(p.O),
-                 "s"(p.w_tiled), "s"(p.ldx), "s"(p.T_in), "s"(p.eps), "s"(fin.norm), "s"(fin.store), "s"(fin.advance),
-                 "s"(p.w), "s"(p.x), "s"(p.w_hn), "s"(p.ss_in), "s"(p.part));
-    const int groups = n_groups / n_splits;
-    const int s = blockIdx.x / groups, t0 = blockIdx.x - s * groups;   // tiles t0 + i*groups
+    // the kernel arguments of the main path in one round of scalar loads (see k_kvfinal)
+    asm volatile("" ::"s"(kp.ntg), "s"(kp.groups), "s"(p.M), "s"(p.nbs), "s"(p.K), "s"(p.O), "s"(p.w_tiled), "s"(p.ldx), "s"(p.T_in),
+                 "s"(p.eps), "s"(fin.norm), "s"(fin.store), "s"(fin.advance), "s"(p.w), "s"(p.x), "s"(p.w_hn),
+                 "s"(p.ss_in), "s"(p.part));
+    // grid (group of the split, split): group t0 of split s takes tiles t0 + i*groups
+    const int groups = kp.groups, s = (int)blockIdx.y, t0 = (int)blockIdx.x;
     // group 0 gathers the rows' and requests' fields, but only for a call that uses them: an
     // unfused projection (no norm, store or advance) may pass no ctx_len_in at all
-    const bool book = blockIdx.x == 0 && (fin.norm || fin.store || fin.advance);
+    const bool book = blockIdx.x == 0 && blockIdx.y == 0 && (fin.norm || fin.store || fin.advance);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
     const int M = p.M, ntg = kp.ntg;
     const int kb0 = s * p.nbs, kc = p.nbs * 128, ldg = kc + 8;
     const int nbw = p.nbs / WAVES;      // blocks per wave per tile (the same for every wave)
     const int total = ntg * nbw;        // this wave's blocks over the group
+    const float rnbw = 1.0f / (float)nbw;
 
     u32x4 a[D][4];
     // this lane's 16-byte piece u of k-block kb of tile t = t0 + i*groups: row t*16 + c16, columns
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     const uint16_t *wl = p.w_tiled ? p.w + (q * 16 + c16) * 8 : p.w + (int64_t)(t0 * 16 + c16) * p.K + q * 8;
     const int w_u = p.w_tiled ? 512 : 32;
     auto load = [&](int slot, int f) {
-        const int i = f / nbw, j = f - (f / nbw) * nbw;
+        const int i = div_small(f, rnbw), j = f - i * nbw;
         const int64_t kb = kb0 + wave + j * WAVES;
         const uint16_t *wp = p.w_tiled ? wl + stream_block(kb, t0 + (int64_t)i * groups, p.O, p.K) * 2048
                                        : wl + (int64_t)i * groups * 16 * p.K + kb * 128;
@@ -333,12 +334,13 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
         }
     }
     const int c8n = kc >> 3;
+    const float rc8n = 1.0f / (float)c8n;
     u32x4 fv[kStageChunks], wv[kStageChunks];
 #pragma unroll
     for (int i = 0; i < kStageChunks; ++i) {
         const int idx = tid + i * NT;
         if (idx < M * c8n) {
-            const int n = idx / c8n, c8 = idx - (idx / c8n) * c8n;
+            const int n = div_small(idx, rc8n), c8 = idx - n * c8n;
             const int64_t kk = (int64_t)kb0 * 128 + (c8 << 3);
             fv[i] = *(const u32x4 *)(p.x + (int64_t)n * p.ldx + kk);
             wv[i] = *(const u32x4 *)(p.w_hn + kk);
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
     for (int i = 0; i < kStageChunks; ++i) {
         const int idx = tid + i * NT;
         if (idx < M * c8n) {
-            const int n = idx / c8n, c8 = idx - (idx / c8n) * c8n;
+            const int n = div_small(idx, rc8n), c8 = idx - n * c8n;
             const float rinv = sh_rinv[n];
             u32x4 gv;
 #pragma unroll
@@ -442,7 +444,7 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
         for (int d = 0; d < D; ++d) {
             const int f = f0 + d;
             if (f >= total) break;
-            const int i = f / nbw, j = f - (f / nbw) * nbw;
+            const int i = div_small(f, rnbw), j = f - i * nbw;
             const int kl = (wave + j * WAVES) * 128;  // k offset inside the split
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -507,8 +509,9 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     const size_t M = (size_t)p.kv.M;
     const size_t g_bytes = M * (size_t)(p.kv.nbs * 128 + 8) * 2;
     const bool two_per_cu = p.n_groups > kKvSlots / 2;
-    hipError_t e = launch1(two_per_cu ? k_kvgroups<1> : k_kvgroups<2>, dim3((unsigned)p.n_groups), dim3(kKvThreads),
-                           s, p, g_bytes);
+    p.groups = p.n_groups / p.kv.S;
+    hipError_t e = launch1(two_per_cu ? k_kvgroups<1> : k_kvgroups<2>, dim3((unsigned)p.groups, (unsigned)p.kv.S),
+                           dim3(kKvThreads), s, p, g_bytes);
     if (e != hipSuccess) return e;
     // finalize: rows per workgroup such that the unit's partials are one round of loads (2 per
     // thread) and each row has its own wave; LDS: the rows [rows][unit_cols] bf16, the k_norm
@@ -520,7 +523,10 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     p.lds_cs = (int32_t)(p.lds_wk + up16((size_t)p.unit_cols * 2));
     const size_t fin_bytes = (size_t)p.lds_cs + (size_t)rows * (size_t)p.fin.nr.rope_dim * 4;
     const unsigned nrb = (unsigned)((M + rows - 1) / rows);
-    return launch1(k_kvfinal, dim3((unsigned)p.n_units * nrb + 1), dim3(kKvThreads), s, p, fin_bytes);
+    // grid (row block, unit of the layer, layer) and one more layer slice for the bookkeeping outputs
+    const unsigned upl = (unsigned)(p.n_units / p.fin.L);
+    if (upl * (unsigned)p.fin.L != (unsigned)p.n_units) return hipErrorInvalidValue;
+    return launch1(k_kvfinal, dim3(nrb, upl, (unsigned)p.fin.L + 1), dim3(kKvThreads), s, p, fin_bytes);
 }
 
 }  // namespace dfkv

@@ -93,13 +93,14 @@ __global__ __launch_bounds__(kHnpThreads) void k_hidden_norm_packed(const Hidden
     uint16_t *rows = (uint16_t *)hn_lds;                // [R][H] bf16
     __shared__ float ssp[8], rinv_s[4];
     const int R = a.packed;                             // rows per workgroup: 1, 2 or 4
+    const int lgR = R >> 1;                             // log2(R), so that no division by R is needed
     const int H = a.H, cpr = H >> 3;                    // 16-byte chunks per row
     const int n0 = blockIdx.x * R;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     // phase 1: wpr = 8 / R waves per row, each summing every wpr-th run of 64 chunks
-    const int wpr = 8 / R;
+    const int wpr = 8 >> lgR;
     {
-        const int r = wave / wpr, part = wave % wpr;
+        const int r = wave >> (3 - lgR), part = wave & (wpr - 1);
         const int n = n0 + r;
         float ss = 0.f;
         for (int c = part * 64 + lane; c < cpr; c += 64 * wpr) {
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(kHnpThreads) void k_hidden_norm_packed(const Hidden
     const int iters = H >> 6;
     const int64_t b = n0 >> 6, j = (n0 >> 5) & 1, fr0 = n0 & 31;
     for (int p = tid; p < R * cpr; p += kHnpThreads) {
-        const int r = p % R, q = p / R;
+        const int r = p & (R - 1), q = p >> lgR;
         const int fh = q & 1, sl = (q >> 1) & 3, it = q >> 3;
         const int k = 64 * it + 32 * fh + 8 * sl;
         const u32x4 v = *(const u32x4 *)(rows + (int64_t)r * H + k);
