@@ -94,7 +94,6 @@ __device__ __forceinline__ void kvfinal_bookkeeping(const FinalizeParams &p, voi
 // k_norm weights, the rows' cos/sin values and slots, into LDS.  Phase B: one wave per row, the
 // per-head arithmetic of finalize_common.hpp, into kv_out and the pools.
 __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
-    extern __shared__ __attribute__((aligned(16))) uint16_t sh_dyn[];
     const FinalizeParams &p = kp.fin;
     // Kernel arguments are read through the scalar cache, which starts cold in every kernel, and the
     // compiler reads a field where the code first needs it: each such place is a round trip of its
@@ -103,7 +102,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     // together with one wait (measured on MI355X: 0.35 us per step, dense drafter at 4 rows).
     asm volatile("" ::"s"(p.M), "s"(kp.fin_rows), "s"(p.L), "s"(p.O), "s"(p.S), "s"(kp.unit_cols),
                  "s"(p.kind), "s"(p.nkv), "s"(p.per_layer), "s"(p.norm), "s"(p.nr.rope_dim), "s"(p.nr.latent),
-                 "s"(kp.lds_wk), "s"(kp.lds_cs), "s"(p.store), "s"(p.pg));
+                 "s"(p.store), "s"(p.pg), "s"(kp.lds_wk), "s"(kp.lds_cs));
     asm volatile("" ::"s"(kp.book), "s"(p.nr.w_knorm), "s"(p.part), "s"(p.kv_out), "s"(p.sp), "s"(p.ss), "s"(p.sh),
                  "s"(p.nr.eps));
     // grid (row block, unit of the layer, layer), plus the slice z = L whose first workgroup writes the
@@ -129,6 +128,101 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     const int nwk = gqa ? cols : p.nr.latent;
     void *book = kp.book;
 
+    if (gqa) {
+        // GQA: every lane takes one 16-byte chunk of a head of one row (hd/8 lanes per row, 512/hd rows
+        // per wave).  One round of loads straight into registers -- the chunk's split partials, its
+        // k_norm weights, its cos/sin values and the row's slot -- then the arithmetic of
+        // knorm_rope_chunk in registers (the head's sum of squares over its lanes by the first DPP
+        // steps of wave_sum, which give the same bits as wave_sum over the head alone), then the
+        // stores.  No LDS and no barrier: measured on MI355X, 1.1 us off the dense drafter's K/V stage
+        // at 4 rows (the MLA rows below, a whole wave each with two or three chunks per lane, were
+        // 1 us slower this way).
+        const int hd = cols, hq = hd >> 4;
+        const int lgl = __builtin_ctz((unsigned)hd) - 3;                 // log2(lanes per row)
+        const int lpr = 1 << lgl, li = lane & (lpr - 1);
+        if ((wave << (6 - lgl)) >= M) return;                             // a wave with no row
+        const int n = (wave << (6 - lgl)) + (lane >> lgl);                // row inside the block
+        const bool rowok = n < M;
+        const int64_t row = n0 + (rowok ? n : 0);
+        // loads: the row's slot, the chunk's k_norm weights and cos/sin values, its split partials
+        const int64_t slot = rowok && p.store ? book_slot(book)[row] : -1;
+        const u32x4 wv = norm ? *(const u32x4 *)(p.nr.w_knorm + (int64_t)l * nwk + 8 * li) : u32x4{0u, 0u, 0u, 0u};
+        const bool first = li < hq;
+        const int j0 = (first ? li : li - hq) * 8;
+        const f32x4 *cp = (const f32x4 *)(book_cs(book) + row * rot + j0);
+        f32x4 cv[2], sv[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            cv[k] = norm && rowok ? cp[k] : f32x4{0.f, 0.f, 0.f, 0.f};
+            sv[k] = norm && rowok ? cp[(rot >> 3) + k] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        // the chunk's 8 split partial sums, added in split order (SB splits per round of loads)
+        constexpr int SB = 8;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const float *src = p.part + row * O + col0 + 8 * li;
+        for (int s0 = 0; s0 < S; s0 += SB) {
+            f32x4 lo[SB], hi[SB];
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                const bool ld = rowok && s0 + k < S;
+                const f32x4 *q = (const f32x4 *)(src + (int64_t)(s0 + k) * Mall * O);
+                lo[k] = ld ? q[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+                hi[k] = ld ? q[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int k = 0; k < SB; ++k) {
+                if (s0 + k >= S) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc[e] += lo[k][e];
+                    acc[4 + e] += hi[k][e];
+                }
+            }
+        }
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = pack2(acc[2 * e], acc[2 * e + 1]);
+        if (norm) {
+            float ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ss += bf_lo(v[e]) * bf_lo(v[e]) + bf_hi(v[e]) * bf_hi(v[e]);
+            // the head's sum over its lpr lanes: quads, then 8, 16 and 32 lanes
+            ss = dpp_add<0xB1>(ss);
+            ss = dpp_add<0x4E>(ss);
+            if (lpr == 8) ss += __shfl_xor(ss, 4, kWave);
+            if (lpr >= 16) {
+                ss = dpp_add<0x124>(ss);
+                ss = dpp_add<0x128>(ss);
+            }
+            if (lpr == 32) ss += __shfl_xor(ss, 16, kWave);
+            const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / (float)hd) + p.nr.eps);
+            u32x4 w, pw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                w[e] = pack2(bf_lo(wv[e]) * (bf_lo(v[e]) * rinv), bf_hi(wv[e]) * (bf_hi(v[e]) * rinv));
+            // RoPE (NeoX): the partner chunk is hq lanes away, inside the row's lanes
+#pragma unroll
+            for (int e = 0; e < 4; ++e) pw[e] = (uint32_t)__shfl_xor((int)w[e], hq, kWave);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float ul = bf_lo(w[e]), uh = bf_hi(w[e]), pl = bf_lo(pw[e]), ph = bf_hi(pw[e]);
+                const float cl = cv[e >> 1][2 * (e & 1)], ch = cv[e >> 1][2 * (e & 1) + 1];
+                const float sl = sv[e >> 1][2 * (e & 1)], sh = sv[e >> 1][2 * (e & 1) + 1];
+                v[e] = first ? pack2(ul * cl - pl * sl, uh * ch - ph * sh) : pack2(ul * cl + pl * sl, uh * ch + ph * sh);
+            }
+        }
+        if (rowok) {
+            if (p.kv_out) *(u32x4 *)(p.kv_out + row * O + col0 + 8 * li) = v;
+            if (slot >= 0)
+                *(u32x4 *)((is_v ? p.pv[l] : p.pk[l]) + slot_offset(p, slot) + (int64_t)h * p.sh + 8 * li) = v;
+        }
+        return;
+    }
+
+    // MLA: phase A (all threads, one round of loads): the split partials summed in split order and
+    // rounded to bf16, the k_norm weights, the rows' cos/sin values and slots, into LDS.  Phase B:
+    // one wave per row -- the latent norm over the whole wave, the rope part -- into kv_out and the pool.
+    extern __shared__ __attribute__((aligned(16))) uint16_t sh_dyn[];
     uint16_t *y = sh_dyn;                                        // [M][cols] bf16
     uint16_t *wk = (uint16_t *)((char *)sh_dyn + kp.lds_wk);     // [cols]
     float *cs = (float *)((char *)sh_dyn + kp.lds_cs);           // [M][rot]
@@ -205,16 +299,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
         const float *csr = cs + n * rot;
         const int64_t slot = sh_slot[n];
         uint16_t *out = p.kv_out ? p.kv_out + (int64_t)(n0 + n) * O + col0 : nullptr;
-        if (gqa) {
-            const int hd = cols, qh = hd >> 3;   // chunks of the head (<= 32 lanes)
-            uint16_t *d = slot >= 0 ? (is_v ? p.pv[l] : p.pk[l]) + slot_offset(p, slot) + (int64_t)h * p.sh : nullptr;
-            u32x4 v = lane < qh ? *(const u32x4 *)(yr + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
-            if (norm) v = knorm_rope_chunk(v, hd, p.nr.eps, wk, csr, lane);
-            if (lane < qh) {
-                if (out) *(u32x4 *)(out + 8 * lane) = v;
-                if (d) *(u32x4 *)(d + 8 * lane) = v;
-            }
-        } else {
+        {
             const int R = p.nr.latent, qr = R >> 3, qp = rot >> 3;
             uint16_t *d = slot >= 0 ? p.pk[l] + slot_offset(p, slot) : nullptr;
             // latent: up to two chunks per lane (R <= 1024); rinv over all of them
@@ -513,15 +598,16 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     hipError_t e = launch1(two_per_cu ? k_kvgroups<1> : k_kvgroups<2>, dim3((unsigned)p.groups, (unsigned)p.kv.S),
                            dim3(kKvThreads), s, p, g_bytes);
     if (e != hipSuccess) return e;
-    // finalize: rows per workgroup such that the unit's partials are one round of loads (2 per
-    // thread) and each row has its own wave; LDS: the rows [rows][unit_cols] bf16, the k_norm
-    // weights, the rows' cos/sin values
-    int rows = 2 * kKvThreads / p.unit_cols;
-    rows = rows < 1 ? 1 : (rows > kKvWaves ? kKvWaves : rows);
+    // finalize: rows per workgroup.  GQA: each wave holds 512 / hd rows of the head.  MLA: as many rows
+    // as keep the unit's partials one round of loads (2 per thread), each row with its own wave; LDS:
+    // the rows [rows][unit_cols] bf16, the k_norm weights, the rows' cos/sin values
+    const bool gqa = p.fin.kind == DFKV_GQA;
+    int rows = gqa ? kKvWaves * (512 / p.unit_cols) : 2 * kKvThreads / p.unit_cols;
+    if (!gqa) rows = rows < 1 ? 1 : (rows > kKvWaves ? kKvWaves : rows);
     p.fin_rows = rows;
     p.lds_wk = (int32_t)up16((size_t)rows * (size_t)p.unit_cols * 2);
     p.lds_cs = (int32_t)(p.lds_wk + up16((size_t)p.unit_cols * 2));
-    const size_t fin_bytes = (size_t)p.lds_cs + (size_t)rows * (size_t)p.fin.nr.rope_dim * 4;
+    const size_t fin_bytes = gqa ? 0 : (size_t)p.lds_cs + (size_t)rows * (size_t)p.fin.nr.rope_dim * 4;
     const unsigned nrb = (unsigned)((M + rows - 1) / rows);
     // grid (row block, unit of the layer, layer) and one more layer slice for the bookkeeping outputs
     const unsigned upl = (unsigned)(p.n_units / p.fin.L);
