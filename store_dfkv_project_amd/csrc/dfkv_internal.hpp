@@ -226,7 +226,6 @@ struct KvParams {
     int32_t unit_cols;        // output columns per unit (head_dim for GQA, latent + rope for MLA)
     int32_t n_units;          // O / unit_cols
     int32_t fin_rows;         // rows per k_kvfinal workgroup (set by launch_kv)
-    int32_t lds_wk, lds_cs;   // MLA: byte offsets in k_kvfinal's dynamic LDS (set by launch_kv)
 };
 hipError_t launch_kv(const KvParams &p, hipStream_t s);
 size_t kv_book_bytes(int rot);

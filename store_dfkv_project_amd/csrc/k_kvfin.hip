@@ -102,7 +102,7 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     // together with one wait (measured on MI355X: 0.35 us per step, dense drafter at 4 rows).
     asm volatile("" ::"s"(p.M), "s"(kp.fin_rows), "s"(p.L), "s"(p.O), "s"(p.S), "s"(kp.unit_cols),
                  "s"(p.kind), "s"(p.nkv), "s"(p.per_layer), "s"(p.norm), "s"(p.nr.rope_dim), "s"(p.nr.latent),
-                 "s"(p.store), "s"(p.pg), "s"(kp.lds_wk), "s"(kp.lds_cs));
+                 "s"(p.store), "s"(p.pg));
     asm volatile("" ::"s"(kp.book), "s"(p.nr.w_knorm), "s"(p.part), "s"(p.kv_out), "s"(p.sp), "s"(p.ss), "s"(p.sh),
                  "s"(p.nr.eps));
     // grid (row block, unit of the layer, layer), plus the slice z = L whose first workgroup writes the
@@ -219,125 +219,124 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
         return;
     }
 
-    // MLA: phase A (all threads, one round of loads): the split partials summed in split order and
-    // rounded to bf16, the k_norm weights, the rows' cos/sin values and slots, into LDS.  Phase B:
-    // one wave per row -- the latent norm over the whole wave, the rope part -- into kv_out and the pool.
-    extern __shared__ __attribute__((aligned(16))) uint16_t sh_dyn[];
-    uint16_t *y = sh_dyn;                                        // [M][cols] bf16
-    uint16_t *wk = (uint16_t *)((char *)sh_dyn + kp.lds_wk);     // [cols]
-    float *cs = (float *)((char *)sh_dyn + kp.lds_cs);           // [M][rot]
-    __shared__ int64_t sh_slot[kKvMaxRows];
-
-    // phase A, one round of loads: the unit's k_norm weights, the rows' cos/sin values and slots are
-    // issued first (into registers), then the split partials; everything lands in LDS after the
-    // partials' wait (loads issued as separate loops would each wait for their own hop)
-    constexpr int EB = 2;   // elements per thread per round
-    constexpr int SB = 8;   // splits per round
-    constexpr int WKN = 1024 / kKvThreads;               // k_norm weights per thread (nwk <= 1024)
-    constexpr int CSF = kKvWaves * 256 / kKvThreads;     // cos/sin values per thread (<= 8 rows x 256)
-    const int total = M * cols;
-    const float rcols = 1.0f / (float)cols;
-    uint16_t wkv[WKN];
-    float csv[CSF];
-    const uint16_t *wsrc = p.nr.w_knorm + (int64_t)l * nwk;
-    const float *bcs = book_cs(book) + (int64_t)n0 * rot;
-#pragma unroll
-    for (int k = 0; k < WKN; ++k) {
-        const int c = tid + k * kKvThreads;
-        wkv[k] = norm && c < nwk ? wsrc[c] : (uint16_t)0;
-    }
-#pragma unroll
-    for (int k = 0; k < CSF; ++k) {
-        const int e = tid + k * kKvThreads;
-        csv[k] = norm && e < M * rot ? bcs[e] : 0.f;
-    }
-    const int64_t slotv = tid < M && p.store ? book_slot(book)[n0 + tid] : -1;
-    for (int e0 = tid; e0 < total; e0 += EB * kKvThreads) {
-        float acc[EB] = {0.f, 0.f};
-        for (int s0 = 0; s0 < S; s0 += SB) {
-            float v[EB][SB];
-#pragma unroll
-            for (int i = 0; i < EB; ++i) {
-                const int e = e0 + i * kKvThreads;
-                const int n = div_small(e, rcols), c = e - n * cols;
-#pragma unroll
-                for (int k = 0; k < SB; ++k)
-                    v[i][k] = (e < total && s0 + k < S) ? p.part[((int64_t)(s0 + k) * Mall + n0 + n) * O + col0 + c]
-                                                         : 0.f;
-            }
-#pragma unroll
-            for (int i = 0; i < EB; ++i)
-#pragma unroll
-                for (int k = 0; k < SB; ++k)
-                    if (s0 + k < S) acc[i] += v[i][k];
+    // MLA: two waves per row -- one for the latent (lane c holds latent chunks c and c + 64), one for the
+    // rope part (lanes < P/8) -- each with one round of loads straight into registers, then the latent
+    // norm by a wave sum, or the rope part's rotation, and the stores (no LDS, no barrier).
+    {
+        const int R = p.nr.latent, qr = R >> 3, qp = rot >> 3;
+        if ((wave >> 1) >= M) return;                                   // a wave with no row
+        const bool latent = (wave & 1) == 0;
+        const int64_t row = n0 + (wave >> 1);
+        const int64_t slot = p.store ? book_slot(book)[row] : -1;
+        uint16_t *d = slot >= 0 ? p.pk[l] + slot_offset(p, slot) : nullptr;
+        uint16_t *out = p.kv_out ? p.kv_out + row * O + col0 : nullptr;
+        // chunks of this lane: latent c = lane, lane + 64 (R <= 1024); rope part c = qr + lane
+        int64_t cc[2];
+        bool ok[2];
+        if (latent) {
+            cc[0] = lane; cc[1] = lane + 64;
+            ok[0] = lane < qr; ok[1] = lane + 64 < qr;
+        } else {
+            cc[0] = qr + lane; cc[1] = 0;
+            ok[0] = lane < qp; ok[1] = false;
         }
+        u32x4 wv[2] = {u32x4{0u, 0u, 0u, 0u}, u32x4{0u, 0u, 0u, 0u}};
+        f32x4 cv[2], sv[2];
+        if (latent) {
 #pragma unroll
-        for (int i = 0; i < EB; ++i) {
-            const int e = e0 + i * kKvThreads;
-            if (e < total) y[e] = f2bf(acc[i]);
+            for (int k = 0; k < 2; ++k)
+                if (norm && ok[k]) wv[k] = *(const u32x4 *)(p.nr.w_knorm + (int64_t)l * nwk + 8 * cc[k]);
         }
-    }
-    if (norm) {
-#pragma unroll
-        for (int k = 0; k < WKN; ++k) {
-            const int c = tid + k * kKvThreads;
-            if (c < nwk) wk[c] = wkv[k];
-        }
-#pragma unroll
-        for (int k = 0; k < CSF; ++k) {
-            const int e = tid + k * kKvThreads;
-            if (e < M * rot) cs[e] = csv[k];
-        }
-    }
-    if (tid < M) sh_slot[tid] = slotv;
-    __syncthreads();
-
-    // phase B: one wave per row, 16-byte chunks (lane L holds elements 8L .. 8L+7 of a head, of the
-    // latent or of the rope part); a NeoX pair's partner chunk is the lane half a head away
-    for (int n = wave; n < M; n += kKvWaves) {
-        const uint16_t *yr = y + n * cols;
-        const float *csr = cs + n * rot;
-        const int64_t slot = sh_slot[n];
-        uint16_t *out = p.kv_out ? p.kv_out + (int64_t)(n0 + n) * O + col0 : nullptr;
+        const int hq = rot >> 4;
+        const bool first = lane < hq;
         {
-            const int R = p.nr.latent, qr = R >> 3, qp = rot >> 3;
-            uint16_t *d = slot >= 0 ? p.pk[l] + slot_offset(p, slot) : nullptr;
-            // latent: up to two chunks per lane (R <= 1024); rinv over all of them
-            u32x4 v[2];
-            float ss = 0.f;
+            const int j0 = (first ? lane : lane - hq) * 8;
+            const f32x4 *cp = (const f32x4 *)(book_cs(book) + row * rot + (j0 < (rot >> 1) ? j0 : 0));
+            const bool ld = !latent && norm && lane < qp;
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int c = lane + 64 * k;
-                v[k] = c < qr ? *(const u32x4 *)(yr + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+                cv[k] = ld ? cp[k] : f32x4{0.f, 0.f, 0.f, 0.f};
+                sv[k] = ld ? cp[(rot >> 3) + k] : f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        // the chunks' split partials, added in split order (SB splits per round of loads)
+        constexpr int SB = 8;
+        float acc[2][8];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[k][e] = 0.f;
+        const float *src = p.part + row * O + col0;
+        for (int s0 = 0; s0 < S; s0 += SB) {
+            f32x4 lo[2][SB], hi[2][SB];
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    const bool ld = ok[k] && s0 + j < S;
+                    const f32x4 *q = (const f32x4 *)(src + (int64_t)(s0 + j) * Mall * O + 8 * cc[k]);
+                    lo[k][j] = ld ? q[0] : f32x4{0.f, 0.f, 0.f, 0.f};
+                    hi[k][j] = ld ? q[1] : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+#pragma unroll
+                for (int j = 0; j < SB; ++j) {
+                    if (s0 + j >= S) break;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[k][e] += lo[k][j][e];
+                        acc[k][4 + e] += hi[k][j][e];
+                    }
+                }
+        }
+        u32x4 v[2];
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[k][e] = pack2(acc[k][2 * e], acc[k][2 * e + 1]);
+        if (latent) {
+            // rinv over both chunks of every lane (zeros where there is none)
+            float ss = 0.f;
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) ss += bf_lo(v[k][e]) * bf_lo(v[k][e]) + bf_hi(v[k][e]) * bf_hi(v[k][e]);
-            }
             if (norm) {
                 ss = wave_sum(ss);
                 const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / (float)R) + p.nr.eps);
 #pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int c = lane + 64 * k;
-                    if (c >= qr) continue;
-                    const u32x4 wv = *(const u32x4 *)(wk + 8 * c);
+                for (int k = 0; k < 2; ++k)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        v[k][e] = pack2(bf_lo(wv[e]) * (bf_lo(v[k][e]) * rinv), bf_hi(wv[e]) * (bf_hi(v[k][e]) * rinv));
-                }
+                        v[k][e] = pack2(bf_lo(wv[k][e]) * (bf_lo(v[k][e]) * rinv), bf_hi(wv[k][e]) * (bf_hi(v[k][e]) * rinv));
             }
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const int c = lane + 64 * k;
-                if (c >= qr) continue;
-                if (out) *(u32x4 *)(out + 8 * c) = v[k];
-                if (d) *(u32x4 *)(d + 8 * c) = v[k];
+                if (!ok[k]) continue;
+                if (out) *(u32x4 *)(out + 8 * cc[k]) = v[k];
+                if (d) *(u32x4 *)(d + 8 * cc[k]) = v[k];
             }
-            // rope part: qp chunks (8 or 16 lanes), rotated without a norm
-            u32x4 r = lane < qp ? *(const u32x4 *)(yr + R + 8 * lane) : u32x4{0u, 0u, 0u, 0u};
-            if (norm) r = rope_chunk(r, rot, csr, lane);
-            if (lane < qp) {
-                if (out) *(u32x4 *)(out + R + 8 * lane) = r;
-                if (d) *(u32x4 *)(d + R + 8 * lane) = r;
+        } else {
+            // the rope part, rotated without a norm (NeoX: the partner chunk is hq lanes away)
+            if (norm) {
+                u32x4 pw;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pw[e] = (uint32_t)__shfl_xor((int)v[0][e], hq, kWave);
+                if (lane < 2 * hq) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float ul = bf_lo(v[0][e]), uh = bf_hi(v[0][e]), pl = bf_lo(pw[e]), ph = bf_hi(pw[e]);
+                        const float cl = cv[e >> 1][2 * (e & 1)], ch = cv[e >> 1][2 * (e & 1) + 1];
+                        const float sl = sv[e >> 1][2 * (e & 1)], sh = sv[e >> 1][2 * (e & 1) + 1];
+                        v[0][e] = first ? pack2(ul * cl - pl * sl, uh * ch - ph * sh)
+                                        : pack2(ul * cl + pl * sl, uh * ch + ph * sh);
+                    }
+                }
+            }
+            if (ok[0]) {
+                if (out) *(u32x4 *)(out + 8 * cc[0]) = v[0];
+                if (d) *(u32x4 *)(d + 8 * cc[0]) = v[0];
             }
         }
     }
@@ -598,21 +597,15 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     hipError_t e = launch1(two_per_cu ? k_kvgroups<1> : k_kvgroups<2>, dim3((unsigned)p.groups, (unsigned)p.kv.S),
                            dim3(kKvThreads), s, p, g_bytes);
     if (e != hipSuccess) return e;
-    // finalize: rows per workgroup.  GQA: each wave holds 512 / hd rows of the head.  MLA: as many rows
-    // as keep the unit's partials one round of loads (2 per thread), each row with its own wave; LDS:
-    // the rows [rows][unit_cols] bf16, the k_norm weights, the rows' cos/sin values
-    const bool gqa = p.fin.kind == DFKV_GQA;
-    int rows = gqa ? kKvWaves * (512 / p.unit_cols) : 2 * kKvThreads / p.unit_cols;
-    if (!gqa) rows = rows < 1 ? 1 : (rows > kKvWaves ? kKvWaves : rows);
+    // finalize: rows per workgroup -- each wave holds 512 / hd rows of a GQA head; an MLA row takes two
+    // waves (latent, rope part)
+    const int rows = p.fin.kind == DFKV_GQA ? kKvWaves * (512 / p.unit_cols) : kKvWaves / 2;
     p.fin_rows = rows;
-    p.lds_wk = (int32_t)up16((size_t)rows * (size_t)p.unit_cols * 2);
-    p.lds_cs = (int32_t)(p.lds_wk + up16((size_t)p.unit_cols * 2));
-    const size_t fin_bytes = gqa ? 0 : (size_t)p.lds_cs + (size_t)rows * (size_t)p.fin.nr.rope_dim * 4;
     const unsigned nrb = (unsigned)((M + rows - 1) / rows);
     // grid (row block, unit of the layer, layer) and one more layer slice for the bookkeeping outputs
     const unsigned upl = (unsigned)(p.n_units / p.fin.L);
     if (upl * (unsigned)p.fin.L != (unsigned)p.n_units) return hipErrorInvalidValue;
-    return launch1(k_kvfinal, dim3(nrb, upl, (unsigned)p.fin.L + 1), dim3(kKvThreads), s, p, fin_bytes);
+    return launch1(k_kvfinal, dim3(nrb, upl, (unsigned)p.fin.L + 1), dim3(kKvThreads), s, p);
 }
 
 }  // namespace dfkv
