@@ -26,10 +26,10 @@
 // that no dependent load sits on the step's tail.
 //
 // k_kvfinal: one workgroup per unit -- a GQA K or V head, or an MLA layer's
-// latent + rope -- and block of rows: one round of loads (the unit's split partials, its k_norm
-// weights, the rows' cos/sin values and slots), then the per-head arithmetic of
-// finalize_common.hpp into kv_out and the pools; one more workgroup writes the
-// bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
+// latent + rope -- and block of rows: one round of loads straight into registers
+// (each lane's chunks of the split partials, their k_norm weights and cos/sin
+// values, the row's slot), then the per-head arithmetic of finalize_common.hpp
+// into kv_out and the pools; one more workgroup writes the bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
 // inside the GEMM kernel by the last arriving group: there every dependent hop
 // (store drain, arrival atomic, partial loads) waited behind the weight stream.
 #include "finalize_common.hpp"
@@ -89,10 +89,7 @@ __device__ __forceinline__ void kvfinal_bookkeeping(const FinalizeParams &p, voi
 }
 
 // Unit u (a GQA K or V head: columns [u*hd, (u+1)*hd); an MLA layer: latent + rope) for the rows
-// [n0, n0 + rpw) -- as many rows as keep the unit's partials one round of loads.  Phase A (all
-// threads, one round of loads): the split partials summed in split order and rounded to bf16, the
-// k_norm weights, the rows' cos/sin values and slots, into LDS.  Phase B: one wave per row, the
-// per-head arithmetic of finalize_common.hpp, into kv_out and the pools.
+// [n0, n0 + fin_rows): GQA rows 512/hd to a wave, MLA rows two waves each (below).
 __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     const FinalizeParams &p = kp.fin;
     // Kernel arguments are read through the scalar cache, which starts cold in every kernel, and the
