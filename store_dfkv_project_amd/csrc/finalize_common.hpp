@@ -134,49 +134,6 @@ __device__ __forceinline__ void knorm_rope_head(const float a[2], const float b[
     }
 }
 
-// NeoX RoPE of a head (or rope part) of `rot` elements held as 16-byte chunks by the first rot/8
-// lanes of a wave (lane L: elements 8L .. 8L+7; every lane of the wave takes part in the exchange).
-// u holds the rounded values; c/s the position's cos and sin halves (cs[0 .. rot/2), cs[rot/2 ..)).
-//   k[j] = bf16(u[j] c_j - u[j+h] s_j),  k[j+h] = bf16(u[j+h] c_j + u[j] s_j)
-__device__ __forceinline__ u32x4 rope_chunk(u32x4 u, int rot, const float *cs, int lane) {
-    const int hq = rot >> 4;   // lanes per half
-    u32x4 pu;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pu[e] = (uint32_t)__shfl_xor((int)u[e], hq, kWave);
-    const bool first = lane < hq;
-    const int j0 = (first ? lane : lane - hq) * 8;
-    if (lane >= 2 * hq) return u;
-    const float *c = cs + j0, *sn = cs + (rot >> 1) + j0;
-    u32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const float ul = bf_lo(u[e]), uh = bf_hi(u[e]), pl = bf_lo(pu[e]), ph = bf_hi(pu[e]);
-        const float cl = c[2 * e], ch = c[2 * e + 1], sl = sn[2 * e], sh = sn[2 * e + 1];
-        o[e] = first ? pack2(ul * cl - pl * sl, uh * ch - ph * sh) : pack2(ul * cl + pl * sl, uh * ch + ph * sh);
-    }
-    return o;
-}
-
-// k_norm then RoPE of a GQA K head of hd elements held as 16-byte chunks by the first hd/8 lanes of a
-// wave (lane L: y[8L .. 8L+7]; zeros in the other lanes, all of which take part in the exchanges):
-//   u = bf16(w * y / sqrt(mean(y^2) + eps)), then rope_chunk.
-__device__ __forceinline__ u32x4 knorm_rope_chunk(u32x4 v, int hd, float eps, const uint16_t *wk, const float *cs,
-                                                  int lane) {
-    float ss = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ss += bf_lo(v[e]) * bf_lo(v[e]) + bf_hi(v[e]) * bf_hi(v[e]);
-    ss = wave_sum(ss);
-    const float rinv = __builtin_amdgcn_rsqf(ss * (1.0f / (float)hd) + eps);
-    u32x4 u = v;
-    if (lane < (hd >> 3)) {
-        const u32x4 wv = *(const u32x4 *)(wk + 8 * lane);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            u[e] = pack2(bf_lo(wv[e]) * (bf_lo(v[e]) * rinv), bf_hi(wv[e]) * (bf_hi(v[e]) * rinv));
-    }
-    return rope_chunk(u, hd, cs, lane);
-}
-
 // 1/rms of an MLA latent held by one wave (v[q2] = y[lane + 64*q2], zeros past the latent).
 __device__ __forceinline__ float latent_rinv(const float v[16], int R, float eps) {
     float ss = 0.f;

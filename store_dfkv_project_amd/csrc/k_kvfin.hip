@@ -28,8 +28,8 @@
 // k_kvfinal: one workgroup per unit -- a GQA K or V head, or an MLA layer's
 // latent + rope -- and block of rows: one round of loads straight into registers
 // (each lane's chunks of the split partials, their k_norm weights and cos/sin
-// values, the row's slot), then the per-head arithmetic of finalize_common.hpp
-// into kv_out and the pools; one more workgroup writes the bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
+// values, the row's slot), then the per-head arithmetic (the rounding points of
+// knorm_rope_head in finalize_common.hpp) into kv_out and the pools; one more workgroup writes the bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
 // inside the GEMM kernel by the last arriving group: there every dependent hop
 // (store drain, arrival atomic, partial loads) waited behind the weight stream.
 #include "finalize_common.hpp"
@@ -128,8 +128,9 @@ __global__ __launch_bounds__(kKvThreads) void k_kvfinal(const KvParams kp) {
     if (gqa) {
         // GQA: every lane takes one 16-byte chunk of a head of one row (hd/8 lanes per row, 512/hd rows
         // per wave).  One round of loads straight into registers -- the chunk's split partials, its
-        // k_norm weights, its cos/sin values and the row's slot -- then the arithmetic of
-        // knorm_rope_chunk in registers (the head's sum of squares over its lanes by the first DPP
+        // k_norm weights, its cos/sin values and the row's slot -- then, in registers, the arithmetic
+        // of knorm_rope_head (u = bf16(w y / rms), k = bf16(u c -/+ u' s) with the NeoX partner u' of
+        // the other half of the head; the head's sum of squares over its lanes by the first DPP
         // steps of wave_sum, which give the same bits as wave_sum over the head alone), then the
         // stores.  No LDS and no barrier: measured on MI355X, 1.1 us off the dense drafter's K/V stage
         // at 4 rows (the MLA rows below, a whole wave each with two or three chunks per lane, were
@@ -577,8 +578,6 @@ __global__ __launch_bounds__(kKvThreads) __attribute__((amdgpu_waves_per_eu(kKvW
 }
 
 size_t kv_book_bytes(int rot) { return (size_t)kKvBookCs + (size_t)kKvMaxRows * (size_t)rot * 4; }
-
-static size_t up16(size_t x) { return (x + 15) & ~(size_t)15; }
 
 hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     if (params.fin.M <= 0) return hipSuccess;
