@@ -29,9 +29,11 @@
 // latent + rope -- and block of rows: one round of loads straight into registers
 // (each lane's chunks of the split partials, their k_norm weights and cos/sin
 // values, the row's slot), then the per-head arithmetic (the rounding points of
-// knorm_rope_head in finalize_common.hpp) into kv_out and the pools; one more workgroup writes the bookkeeping outputs.  Measured on MI355X, this is faster than finalizing
-// inside the GEMM kernel by the last arriving group: there every dependent hop
-// (store drain, arrival atomic, partial loads) waited behind the weight stream.
+// knorm_rope_head in finalize_common.hpp) into kv_out and the pools; one more
+// workgroup writes the bookkeeping outputs.  Measured on MI355X, this is faster
+// than finalizing inside the GEMM kernel by the last arriving group: there every
+// dependent hop (store drain, arrival atomic, partial loads) waited behind the
+// weight stream.
 #include "finalize_common.hpp"
 
 namespace dfkv {
