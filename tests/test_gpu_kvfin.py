@@ -32,6 +32,11 @@ CASES = [
     # latent of 1024 (two 16-byte chunks per lane) and a rope part of 128 (a latent of 448)
     (19, MLA, 2, 4, 8, "nhd", 2, 1, 0, 1, 1024, 1024, 1024, 64),
     (20, MLA, 3, 4, 8, "nhd", 2, 1, 0, 2, 512, 1024, 448, 128),
+    # rows that fill part of a wave of the finishing kernel: hd 64 (8 rows a wave) with 5 rows, hd 256
+    # (2 rows a wave) with 3, one MLA row with a latent of 1024 (two latent chunks a lane)
+    (22, GQA, 5, 1, 4, "hnd", 2, 2, 64, 2, 1024, 2048),
+    (23, GQA, 1, 3, 2, "nhd", 3, 1, 256, 1, 1536, 1024),
+    (24, MLA, 1, 1, 4, "nhd", 2, 1, 0, 1, 1024, 1024, 1024, 64),
 ]
 
 
