@@ -218,14 +218,19 @@ def parity_record(gpu: dict, rows, ref_kv, ref_book: dict) -> dict:
 def measure_overlap(ds, stream, R, per_graph, timed, n_rep, window_us) -> dict:
     """The projection forked onto an aux stream ahead of a simulated sample/accept window (a spin kernel
     of about `window_us` on the main stream) and joined before the store, against the same three pieces
-    in series on one stream (the overlap switch of the PR #20550 page).  Both captured in graphs of
-    `per_graph` consecutive steps rotating over the weight copies."""
+    in series on one stream (the overlap switch of the PR #20550 page).  All captured in graphs of
+    `per_graph` consecutive steps rotating over the weight copies.  Two capture orders of the same
+    dependencies: the fork point recorded first and the window queued before the projection's launch
+    (DFKV_FORK_RECORDED; the headline), and the projection forked at the call, ahead of the window."""
     import torch
     from store_dfkv_project_amd import dfkv
     aux = torch.cuda.Stream()
     fork, join = torch.cuda.Event(), torch.cuda.Event()
     fork.record(stream)
     join.record(aux)
+    fork2, join2 = torch.cuda.Event(), torch.cuda.Event()
+    fork2.record(stream)
+    join2.record(aux)
     torch.cuda.synchronize()
 
     def spin_cycles(us):
@@ -255,24 +260,38 @@ def measure_overlap(ds, stream, R, per_graph, timed, n_rep, window_us) -> dict:
         ds.store_advance(stream=stream)
 
     def overlapped(c):
-        ds.project_fork(stream, aux, fork.cuda_event, join.cuda_event, copy=c)
+        # the fork point recorded before the window; the projection queued after it on aux
+        fork.record(stream)
         torch.cuda._sleep(cycles)
+        ds.project_fork(stream, aux, fork.cuda_event, join.cuda_event, copy=c,
+                        flags=dfkv.DFKV_FUSE_NORM_ROPE | dfkv.DFKV_FORK_RECORDED)
         dfkv.dfkv_join(stream, join.cuda_event)
+        ds.store_advance(stream=stream)
+
+    def overlapped_at_call(c):
+        ds.project_fork(stream, aux, fork2.cuda_event, join2.cuda_event, copy=c)
+        torch.cuda._sleep(cycles)
+        dfkv.dfkv_join(stream, join2.cuda_event)
         ds.store_advance(stream=stream)
 
     def window_only(c):
         torch.cuda._sleep(cycles)
 
     g_ser, g_ovl, g_win = capture(serial), capture(overlapped), capture(window_only)
+    g_call = capture(overlapped_at_call)
     torch.cuda.synchronize()
     reps = max(4, n_rep // 2)
     ser = float(timed([g_ser], reps, 1, per_graph).mean())
     ovl = float(timed([g_ovl], reps, 1, per_graph).mean())
     win = float(timed([g_win], reps, 1, per_graph).mean())
+    call = float(timed([g_call], reps, 1, per_graph).mean())
     return {"window_us": round(win, 2), "serial_us_per_step": round(ser, 2),
             "overlapped_us_per_step": round(ovl, 2), "hidden_us_per_step": round(ser - ovl, 2),
+            "overlapped_fork_at_call_us_per_step": round(call, 2),
             "what": "project + simulated sample/accept window + store_advance per step; overlapped: the "
-                    "projection forked onto an aux stream ahead of the window, joined before the store"}
+                    "projection forked onto an aux stream at a fork point recorded ahead of the window "
+                    "(DFKV_FORK_RECORDED, its launch queued after the window's), joined before the store; "
+                    "fork_at_call: the same dependencies with the projection queued ahead of the window"}
 
 
 def measure_bt_decode(stream, timed, B: int = 256, max_blocks: int = 1024) -> dict:

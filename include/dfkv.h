@@ -74,8 +74,8 @@ typedef enum dfkv_status {
 enum { DFKV_GQA = 0, DFKV_MLA = 1 };
 enum { DFKV_MAX_LAYERS = 32 };
 
-/* dfkv_project flags */
-enum { DFKV_FUSE_NORM_ROPE = 1u };
+/* dfkv_project flags (DFKV_FORK_RECORDED: dfkv_project_fork only) */
+enum { DFKV_FUSE_NORM_ROPE = 1u, DFKV_FORK_RECORDED = 2u };
 
 /* Geometry of the drafter and of the step.
  *  GQA: each layer's stacked projection row is [2][n_kv_heads][head_dim]
@@ -455,6 +455,14 @@ dfkv_status dfkv_block_table_decode(const int32_t *offsets, int64_t off_stride_r
  * on `main` reads kv_out or the workspace (dfkv_store_advance).  Streams and
  * events (hipStream_t, hipEvent_t) are the caller's; both calls may be
  * captured into one hipGraph together with the work on `main`.
+ * With DFKV_FORK_RECORDED in `flags` the caller has already recorded `fork` on
+ * `main` at the fork point, and the call only makes `aux` wait for it (`main`
+ * is not used).  The caller may then queue sample/accept on `main` before this
+ * call, so that in a captured graph the main-stream work comes first in
+ * capture order: HIP's graph launch keeps such a graph's first branch, here
+ * the sample/accept work, on one hardware queue, and the later work on `main`
+ * (the store) follows it there instead of the projection, which saves a
+ * cross-queue hand-off per step.
  * Errors: as dfkv_project (nothing queued, no event recorded); NULL for a NULL
  * event; HIP when recording or waiting fails. */
 dfkv_status dfkv_project_fork(const dfkv_geom *g, const dfkv_weights *w, const void *hidden,

@@ -682,11 +682,13 @@ dfkv_status dfkv_project_fork(const dfkv_geom *g, const dfkv_weights *w, const v
                               const float *cos_sin, int32_t cache_len, void *kv_out, uint32_t flags, void *ws,
                               size_t ws_bytes, dfkv_stream_t main, dfkv_stream_t aux, void *fork, void *join) {
     Plan pl;
+    const bool recorded = (flags & DFKV_FORK_RECORDED) != 0;
+    flags &= ~(uint32_t)DFKV_FORK_RECORDED;
     dfkv_status st = check_project(g, w, hidden, hidden_row_stride, n_reqs, ctx_len_in, cos_sin, cache_len, kv_out,
                                    flags, ws, ws_bytes, &pl);
     if (st != DFKV_OK) return st;
     if (!fork || !join) return DFKV_ERR_NULL;
-    hipError_t e = hipEventRecord((hipEvent_t)fork, (hipStream_t)main);
+    hipError_t e = recorded ? hipSuccess : hipEventRecord((hipEvent_t)fork, (hipStream_t)main);
     if (e == hipSuccess) e = hipStreamWaitEvent((hipStream_t)aux, (hipEvent_t)fork, 0);
     if (e != hipSuccess) return hip_status(e);
     const FinalizeParams fin = fin_params(g, nullptr, nullptr, nullptr, n_reqs);

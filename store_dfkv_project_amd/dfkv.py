@@ -32,6 +32,7 @@ DFKV_GQA = 0
 DFKV_MLA = 1
 DFKV_MAX_LAYERS = 32
 DFKV_FUSE_NORM_ROPE = 1
+DFKV_FORK_RECORDED = 2
 
 EXPORTED = ("dfkv_status_string", "dfkv_version", "dfkv_hip_error_string", "dfkv_workspace_size", "dfkv_workspace_init",
             "dfkv_rope_cache_build", "dfkv_project", "dfkv_project_fc", "dfkv_project_kv", "dfkv_norm_rope", "dfkv_paged_store", "dfkv_advance",

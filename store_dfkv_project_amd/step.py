@@ -158,8 +158,9 @@ class DeviceStep:
                           flags, self.ws, self.ws_bytes, stream)
 
     def project_fork(self, main, aux, fork, join, flags: int = dfkv.DFKV_FUSE_NORM_ROPE, copy: int = 0):
-        """The projection on `aux` after the work queued on `main` so far; `join` recorded after it
-        (fork / join: raw hipEvent_t handles)."""
+        """The projection on `aux` after the work queued on `main` so far (with DFKV_FORK_RECORDED in
+        `flags`: after the `fork` the caller recorded); `join` recorded after it (fork / join: raw
+        hipEvent_t handles)."""
         dfkv.dfkv_project_fork(self.gs, self.weight_structs[copy], self.hidden, self.wl.hidden_row_stride,
                                self.wl.n_reqs, self.ctx_len, self.cos_sin, self.cache_len, self.kv_out, flags,
                                self.ws, self.ws_bytes, main, aux, fork, join)

@@ -315,6 +315,12 @@ def test_fork_join_validation():
     assert status_of(dfkv.dfkv_project_fork, **dict(base, join=0)) == dfkv.DFKV_ERR_NULL
     assert status_of(dfkv.dfkv_project_fork, **dict(base, ws_bytes=ws - 256)) == dfkv.DFKV_ERR_WORKSPACE
     assert status_of(dfkv.dfkv_project_fork, **dict(base, kv_out=addr(5))) == dfkv.DFKV_ERR_ALIAS
+    # DFKV_FORK_RECORDED is dfkv_project_fork's alone; other bits stay rejected
+    recorded = dfkv.DFKV_FUSE_NORM_ROPE | dfkv.DFKV_FORK_RECORDED
+    assert status_of(dfkv.dfkv_project_fork, **dict(base, flags=recorded, fork=0)) == dfkv.DFKV_ERR_NULL
+    assert status_of(dfkv.dfkv_project_fork, **dict(base, flags=recorded, ws_bytes=ws - 256)) == \
+        dfkv.DFKV_ERR_WORKSPACE
+    assert status_of(dfkv.dfkv_project_fork, **dict(base, flags=4)) == dfkv.DFKV_ERR_SHAPE
     assert status_of(dfkv.dfkv_join, 0, 0) == dfkv.DFKV_ERR_NULL
 
 

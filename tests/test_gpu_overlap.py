@@ -36,33 +36,47 @@ def _same(a, b):
         assert np.array_equal(ga[k], gb[k]), k
 
 
+def _overlapped(a, main, aux, fork, join, window, recorded):
+    """One overlapped step on `main`: the projection forked at the call, ahead of the window, or
+    (recorded) at a fork point the caller records before the window, the projection queued after it."""
+    import torch
+    from store_dfkv_project_amd import dfkv
+    with torch.cuda.stream(main):
+        if recorded:
+            fork.record(main)
+            torch.cuda._sleep(window)
+            a.project_fork(main, aux, fork.cuda_event, join.cuda_event,
+                           flags=dfkv.DFKV_FUSE_NORM_ROPE | dfkv.DFKV_FORK_RECORDED)
+        else:
+            a.project_fork(main, aux, fork.cuda_event, join.cuda_event)
+            torch.cuda._sleep(window)            # the sample/accept window on main
+        dfkv.dfkv_join(main, join.cuda_event)
+        a.store_advance(stream=main)
+
+
+@pytest.mark.parametrize("recorded", [False, True])
 @pytest.mark.parametrize("cfg", [0, 1])
-def test_fork_join_equals_step(orc, cfg):
+def test_fork_join_equals_step(orc, cfg, recorded):
     import torch
     wl, a, b = _pair(cfg)
-    print(f"[overlap] fork/join config {cfg}", flush=True)
+    print(f"[overlap] fork/join config {cfg} fork recorded by the caller {recorded}", flush=True)
     main, aux = torch.cuda.Stream(), torch.cuda.Stream()
     fork, join = _event(main), _event(aux)
     torch.cuda.synchronize()
-    with torch.cuda.stream(main):
-        a.project_fork(main, aux, fork.cuda_event, join.cuda_event)
-        torch.cuda._sleep(2_000_000)            # the sample/accept window on main
-        from store_dfkv_project_amd import dfkv
-        dfkv.dfkv_join(main, join.cuda_event)
-        a.store_advance(stream=main)
+    _overlapped(a, main, aux, fork, join, 2_000_000, recorded)
     b.step()
     torch.cuda.synchronize()
     _same(a, b)
     compare_bookkeeping(a.outputs_host(), oracle_bookkeeping(orc, wl), f"overlap config {cfg}")
 
 
-def test_fork_join_graph_replays():
+@pytest.mark.parametrize("recorded", [False, True])
+def test_fork_join_graph_replays(recorded):
     """The overlapped step (fork, window, join, store) captured into one graph on `main`: every replay,
     with eager work and synchronisations between replays, gives the eager bits."""
     import torch
-    from store_dfkv_project_amd import dfkv
     wl, a, b = _pair(1)
-    print("[overlap] graph capture", flush=True)
+    print(f"[overlap] graph capture, fork recorded by the caller {recorded}", flush=True)
     main, aux = torch.cuda.Stream(), torch.cuda.Stream()
     fork, join = _event(main), _event(aux)
     b.step()
@@ -70,10 +84,7 @@ def test_fork_join_graph_replays():
     pool0 = a.pool_t.clone()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=main):
-        a.project_fork(main, aux, fork.cuda_event, join.cuda_event)
-        torch.cuda._sleep(200_000)
-        dfkv.dfkv_join(main, join.cuda_event)
-        a.store_advance(stream=main)
+        _overlapped(a, main, aux, fork, join, 200_000, recorded)
     torch.cuda.synchronize()
     for rep in range(3):
         a.pool_t.copy_(pool0)
