@@ -585,8 +585,10 @@ hipError_t launch_kv(const KvParams &params, hipStream_t s) {
     if (params.fin.M <= 0) return hipSuccess;
     KvParams p = params;
     const int tpu = p.unit_cols / 16;
+    // the shapes the kernels index by: g's staging chunks, the row bookkeeping, the cos/sin registers
     if (p.kv.nbs % kKvWaves != 0 || p.kv.nbs <= 0 || p.ntg <= 0 || p.ntg > tpu || p.n_groups % p.kv.S != 0 ||
-        p.fin.M > kKvMaxRows || p.fin.B > kKvMaxRows || p.fin.nr.rope_dim > 256)
+        !stage_fits(p.kv.M, p.kv.nbs) || p.kv.M != p.fin.M || p.fin.M > kKvMaxRows || p.fin.B > kKvMaxRows ||
+        p.fin.nr.rope_dim > 256)
         return hipErrorInvalidValue;
     const size_t M = (size_t)p.kv.M;
     const size_t g_bytes = M * (size_t)(p.kv.nbs * 128 + 8) * 2;
