@@ -4,7 +4,8 @@ projection's.  The shapes are drawn inside what the interface accepts (GQA head 
 full rotation; MLA latent a multiple of 64 up to 1024 with an even rope part up to 128, their sum a
 multiple of 64; hidden sizes multiples of 128) and the row counts span the three paths: up to 16
 rows (split-K groups + finishing kernel), 17 to 64 (streaming GEMMs + finalize) and above 64 (MFMA
-GEMMs, 128- or 256-token tiles).  Each case prints its draw first."""
+GEMMs, 128- or 256-token tiles).  A second, wider draw reaches 32 layers, hidden sizes from 128 to
+8192 and k_in above 20000.  Each case prints its draw first."""
 import dataclasses
 
 import numpy as np
@@ -51,12 +52,62 @@ def _draw(seed):
     return geom, B, rng
 
 
+def _draw_wide(seed):
+    """Wider geometries: up to 32 layers, hidden sizes from 128 to 8192, k_in up to 25600 and up to
+    about 700 rows, with the oracle's work and the pool's size bounded (None outside the bounds)."""
+    rng = np.random.default_rng(77000 + seed)
+    kind = GQA if rng.random() < 0.6 else MLA
+    n_tgt = int(rng.integers(1, 6))
+    tgt_hidden = 128 * int(rng.integers(1, 41))
+    hidden = 128 * int(rng.choice([1, 2, 5, 8, 16, 24, 32, 40, 56, 64]))
+    L = int(rng.choice([1, 2, 3, 7, 12, 16, 32]))
+    W = int(rng.integers(1, 17))
+    target_rows = int(rng.choice([int(rng.integers(1, 17)), int(rng.integers(17, 65)), int(rng.integers(65, 700))]))
+    W = min(W, max(1, target_rows // 5)) if target_rows >= 5 else 1
+    B = max(1, target_rows // W)
+    pg = int(rng.choice([1, 2, 4, 16, 64, 128]))
+    bs = int(rng.integers(1, 17))
+    if kind == GQA:
+        hd = int(rng.choice([64, 128, 256]))
+        nkv = int(rng.choice([1, 2, 4, 8]))
+        geom = small_geom(GQA, L=L, nkv=nkv, hd=hd, pg=pg, W=W, bs=bs, n_tgt=n_tgt, tgt_hidden=tgt_hidden,
+                          hidden=hidden)
+        per_slot = L * 2 * nkv * hd * 2
+    else:
+        R = 64 * int(rng.integers(1, 17))
+        P = int(rng.choice([64, 128]))
+        geom = small_geom(MLA, L=L, R=R, P=P, pg=pg, W=W, bs=bs, n_tgt=n_tgt, tgt_hidden=tgt_hidden, hidden=hidden)
+        per_slot = L * (R + P) * 2
+    if B * W * (geom.k_in * geom.hidden + geom.hidden * geom.out_dim) > 4e10:
+        return None
+    if max(64, 6 * B + 2) * pg * per_slot > 2e9:     # the edge workload's pages, every layer
+        return None
+    return geom, B, rng
+
+
+# wide draws that cover: 32 layers, hidden 128 and 8192, k_in above 20000, a large-batch GQA finalize
+# with more chunks per row than one pass of its workgroup, and each of the three paths
+WIDE_SEEDS = [2, 3, 8, 22, 28, 32, 33, 36, 45, 49, 51, 58, 63, 74, 79, 81, 101, 106, 119]
+
+
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_shape_step(orc, seed):
+    _run(orc, seed, _draw(seed))
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("seed", WIDE_SEEDS)
+def test_wide_shape_step(orc, seed):
+    drawn = _draw_wide(seed)
+    assert drawn is not None
+    _run(orc, seed, drawn)
+
+
+def _run(orc, seed, drawn):
     import torch
     from store_dfkv_project_amd.step import DeviceStep
-    geom, B, rng = _draw(seed)
+    geom, B, rng = drawn
     print(f"[random] seed {seed}: kind={'GQA' if geom.kind == GQA else 'MLA'} k_in={geom.k_in} H={geom.hidden} "
           f"L={geom.n_layers} O={geom.out_dim} W={geom.width} B={B} rows={B * geom.width} pg={geom.page_size} "
           f"block={geom.block_size}", flush=True)
